@@ -1,0 +1,268 @@
+"""Benchmark of the FP8 block-scaled NT GEMM on one MI355X.
+
+A step is one call of the GEMM entry point (tile scheduling, operand and
+scale staging, FP8 MFMA per 128-wide K block, promotion, bf16 epilogue) on
+inputs already quantized and resident in HBM.  The default workload is the
+dense M=4096, N=7168, K=2048 projection.  Inputs rotate over enough copies
+(more than 512 MiB in total) that the 256 MiB last-level cache cannot serve
+them from one step to the next.
+
+Prints one JSON line:
+  value        TFLOPS over the timed steps (2*rows*N*K per step / wall time)
+  roofline     the GEMM kernel against the dense FP8 MFMA peak (or HBM for
+               bandwidth-bound workloads), from HIP events around each launch
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+ROTATE_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dense_4096x7168x2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic(case):
+    """FLOP and HBM bytes the method must move per call (unrouted rows and
+    groups without rows excluded)."""
+    rows = case.valid_rows
+    KB, NB = case.K // 128, (case.N + 127) // 128
+    flop = 2.0 * rows * case.N * case.K
+    groups = case.active_groups
+    byts = (rows * case.K                     # A codes
+            + groups * case.N * case.K        # B codes of groups in use
+            + 4 * (rows * KB + groups * NB * KB)   # scales
+            + 2 * rows * case.N)              # bf16 D
+    return flop, float(byts)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_block_scaled_gemm_amd", "csrc")
+    for f in ("gemm.hip", "device_common.h", "launch.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def make_inputs(case, dev, dg):
+    import torch
+    x_a = case.x_a.to(dev)
+    x_b = case.x_b.to(dev)
+    K = case.K
+    qa, sa = dg.dg_quantize_fp8_per_token(x_a.reshape(-1, K))
+    qa = qa.reshape(x_a.shape)
+    sa = sa.reshape(*x_a.shape[:-1], K // 128)
+    if x_b.dim() == 2:
+        qb, sb = dg.dg_quantize_fp8_per_block(x_b)
+    else:
+        parts = [dg.dg_quantize_fp8_per_block(x_b[g].contiguous()) for g in range(x_b.shape[0])]
+        qb = torch.stack([p[0] for p in parts])
+        sb = torch.stack([p[1] for p in parts])
+    aux = None
+    if case.form == "contiguous":
+        aux = case.layout.to(dev)
+    elif case.form == "masked":
+        aux = case.masked_m.to(dev)
+    if case.form == "masked":
+        D = torch.empty((case.G, case.M, case.N), dtype=torch.bfloat16, device=dev)
+    else:
+        D = torch.empty((case.M, case.N), dtype=torch.bfloat16, device=dev)
+    return {"A": qa, "sa": sa, "B": qb, "sb": sb, "D": D, "aux": aux, "x_a": x_a, "x_b": x_b}
+
+
+def gemm_call(case, dg, t):
+    if case.form == "dense":
+        dg.dg_fp8_gemm_nt(t["A"], t["sa"], t["B"], t["sb"], t["D"])
+    elif case.form == "contiguous":
+        dg.dg_fp8_gemm_grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
+    else:
+        dg.dg_fp8_gemm_grouped_masked(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
+
+
+def time_quantize(dg, t, case, reps=20):
+    """Average time of the per-token quantization of A (the activation side,
+    re-done every step in use) with HIP events; reported beside the GEMM."""
+    import torch
+    x = t["x_a"].reshape(-1, case.K)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty((x.shape[0], case.K // 128), dtype=torch.float32, device=x.device)
+    for _ in range(3):
+        dg.dg_quantize_fp8_per_token(x, q, s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dg.dg_quantize_fp8_per_token(x, q, s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    byts = x.numel() * 5 + s.numel() * 4
+    return {"kernel": "quantize_per_token", "rows": int(x.shape[0]), "K": case.K,
+            "us": round(ms * 1e3, 2), "GB/s": round(byts / (ms * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline(case, target_s: float):
+    """The CPU oracle (untuned) on a bounded sample of rows of the same
+    workload; TFLOPS scaled to the sample's own FLOP count."""
+    import numpy as np
+    import oracle
+
+    K = case.K
+    xa = case.x_a.reshape(-1, K).numpy()
+    if case.form == "dense":
+        qb, sb = oracle.quantize_per_block(case.x_b.numpy())
+        routed = np.arange(case.M)
+    elif case.form == "contiguous":
+        parts = [oracle.quantize_per_block(np.ascontiguousarray(case.x_b[g].numpy()))
+                 for g in range(case.G)]
+        qb = np.stack([p[0] for p in parts]); sb = np.stack([p[1] for p in parts])
+        lay = case.layout.numpy()
+        routed = np.nonzero((lay >= 0) & (lay < case.G))[0]
+    else:
+        parts = [oracle.quantize_per_block(np.ascontiguousarray(case.x_b[g].numpy()))
+                 for g in range(case.G)]
+        qb = np.stack([p[0] for p in parts]); sb = np.stack([p[1] for p in parts])
+        mm = np.clip(case.masked_m.numpy(), 0, case.M)
+        routed = np.concatenate([g * case.M + np.arange(mm[g]) for g in range(case.G)])
+    qa, sa = oracle.quantize_per_token(xa)
+
+    def run(rows):
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        t0 = time.perf_counter()
+        if case.form == "dense":
+            oracle.gemm_nt(qa, sa, qb, sb, rows=rows)
+        elif case.form == "contiguous":
+            oracle.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=rows)
+        else:
+            oracle.gemm_grouped_masked(qa.reshape(case.G, case.M, K), sa.reshape(case.G, case.M, -1),
+                                       qb, sb, case.masked_m.numpy(), rows=rows)
+        return time.perf_counter() - t0
+
+    threads = oracle.num_threads()
+    probe = routed[:max(threads, 8)]
+    t_probe = run(probe)
+    per_row = t_probe / len(probe)
+    n_rows = int(min(len(routed), max(len(probe), target_s / max(per_row, 1e-9))))
+    sample = routed[np.linspace(0, len(routed) - 1, n_rows).astype(np.int64)]
+    t = run(sample)
+    flop = 2.0 * len(sample) * case.N * K
+    return {"value": round(flop / t / 1e12, 5), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(sample)} of {len(routed)} routed rows of {case.name} "
+                      f"(all N={case.N} columns, K={K}), {t:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of this path is a design note, not a measured path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_gemm_amd as dg
+    from fp8_block_scaled_gemm_amd.inputs import workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = workload(args.workload)
+    flop, byts = algorithmic(case)
+    base = make_inputs(case, dev, dg)
+    torch.cuda.synchronize()
+
+    in_bytes = sum(base[k].numel() * base[k].element_size() for k in ("A", "sa", "B", "sb", "D"))
+    copies = max(1, -(-ROTATE_BYTES // in_bytes))
+    sets = [base]
+    for _ in range(copies - 1):
+        sets.append({k: (v.clone() if (v is not None and k not in ("x_a", "x_b")) else v)
+                     for k, v in base.items()})
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        gemm_call(case, dg, sets[i % copies])
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        gemm_call(case, dg, sets[i % copies])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    intensity = flop / byts
+    if intensity >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flop / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    else:
+        achieved = byts / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic_from_profiles(case.name)
+    roof["kernel"] = f"gemm_kernel ({case.form})"
+    roof["kernel_us"] = round(kernel_ms * 1e3, 2)
+    roof["algorithmic_flop"] = flop
+    roof["algorithmic_bytes"] = byts
+
+    quant = time_quantize(dg, base, case)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOPS (and % of FP8 MFMA peak) at M=4096,N=7168,K=2048",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": case.name, "form": case.form, "M": case.M, "N": case.N,
+                   "K": case.K, "G": case.G, "valid_rows": case.valid_rows,
+                   "rotated_input_sets": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "quantize": quant,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,118 @@
+// The library's C ABI (declared in include/dg_fp8.h): host-side argument
+// checks, then one enqueue on the caller's stream.  Nothing here touches the
+// GPU before every check has passed, so a rejected call enqueues nothing.
+#include "dg_fp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool product_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
+
+// Checks shared by the three GEMM forms.
+dg_status check_nk(int64_t N, int64_t K) {
+    if (N <= 0 || N % 8 != 0) return DG_ERR_SHAPE;
+    if (K <= 0 || K % 128 != 0) return DG_ERR_SHAPE;
+    if (!product_ok(N, K)) return DG_ERR_SHAPE;
+    if (N > 0x7fffffffLL || K > 0x7fffffffLL) return DG_ERR_SHAPE;
+    return DG_OK;
+}
+
+dg_status check_ptrs(const void* const* ptrs, int n) {
+    for (int i = 0; i < n; ++i)
+        if (ptrs[i] == nullptr) return DG_ERR_NULL;
+    for (int i = 0; i < n; ++i)
+        if (!aligned16(ptrs[i])) return DG_ERR_ALIGN;
+    return DG_OK;
+}
+
+dg_status from_hip(hipError_t e) { return e == hipSuccess ? DG_OK : DG_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                         uint16_t* D, int64_t M, int64_t N, int64_t K, void* stream) {
+    dg_status s = check_nk(N, K);
+    if (s != DG_OK) return s;
+    if (M < 0 || !product_ok(M, K) || !product_ok(M, N) || M > 0x7fffffffLL) return DG_ERR_SHAPE;
+    if (M == 0) return DG_OK;
+    const void* ptrs[] = {A, sa, B, sb, D};
+    if ((s = check_ptrs(ptrs, 5)) != DG_OK) return s;
+    dg::GemmArgs a{A, sa, B, sb, D, nullptr, M, N, K, 1};
+    return from_hip(dg::launch_gemm(dg::Form::Dense, a, static_cast<hipStream_t>(stream)));
+}
+
+dg_status dg_fp8_gemm_grouped_contiguous(const uint8_t* A, const float* sa, const uint8_t* B,
+                                         const float* sb, uint16_t* D,
+                                         const int32_t* grouped_layout, int64_t M_sum, int64_t N,
+                                         int64_t K, int64_t G, void* stream) {
+    dg_status s = check_nk(N, K);
+    if (s != DG_OK) return s;
+    if (G < 1 || G > 0x7fffffffLL || !product_ok(G, N * K)) return DG_ERR_SHAPE;
+    if (M_sum < 0 || M_sum % 128 != 0 || M_sum > 0x7fffffffLL) return DG_ERR_SHAPE;
+    if (!product_ok(M_sum, K) || !product_ok(M_sum, N)) return DG_ERR_SHAPE;
+    if (M_sum == 0) return DG_OK;
+    const void* ptrs[] = {A, sa, B, sb, D, grouped_layout};
+    if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
+    dg::GemmArgs a{A, sa, B, sb, D, grouped_layout, M_sum, N, K, G};
+    return from_hip(dg::launch_gemm(dg::Form::Contiguous, a, static_cast<hipStream_t>(stream)));
+}
+
+dg_status dg_fp8_gemm_grouped_masked(const uint8_t* A, const float* sa, const uint8_t* B,
+                                     const float* sb, uint16_t* D, const int32_t* masked_m,
+                                     int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                     void* stream) {
+    dg_status s = check_nk(N, K);
+    if (s != DG_OK) return s;
+    if (G < 1 || G > 0x7fffffffLL || !product_ok(G, N * K)) return DG_ERR_SHAPE;
+    if (M_max < 0 || M_max > 0x7fffffffLL) return DG_ERR_SHAPE;
+    if (!product_ok(G * M_max, K) || !product_ok(G * M_max, N)) return DG_ERR_SHAPE;
+    if (M_max == 0) return DG_OK;
+    const void* ptrs[] = {A, sa, B, sb, D, masked_m};
+    if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
+    dg::GemmArgs a{A, sa, B, sb, D, masked_m, M_max, N, K, G};
+    return from_hip(dg::launch_gemm(dg::Form::Masked, a, static_cast<hipStream_t>(stream)));
+}
+
+dg_status dg_quantize_fp8_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                                    void* stream) {
+    if (K <= 0 || K % 128 != 0 || M < 0 || !product_ok(M, K)) return DG_ERR_SHAPE;
+    if (M == 0) return DG_OK;
+    const void* ptrs[] = {x, q, s};
+    dg_status st = check_ptrs(ptrs, 3);
+    if (st != DG_OK) return st;
+    return from_hip(dg::launch_quantize_per_token(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
+dg_status dg_quantize_fp8_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
+                                    void* stream) {
+    if (K <= 0 || K % 128 != 0 || N < 0 || !product_ok(N, K)) return DG_ERR_SHAPE;
+    if ((N + 127) / 128 > 65535) return DG_ERR_SHAPE;
+    if (N == 0) return DG_OK;
+    const void* ptrs[] = {x, q, s};
+    dg_status st = check_ptrs(ptrs, 3);
+    if (st != DG_OK) return st;
+    return from_hip(dg::launch_quantize_per_block(x, N, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
+const char* dg_status_string(dg_status status) {
+    switch (status) {
+        case DG_OK: return "ok";
+        case DG_ERR_NULL: return "a required pointer is NULL";
+        case DG_ERR_SHAPE: return "a size is out of range";
+        case DG_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case DG_ERR_UNSUPPORTED: return "arguments are valid but not supported by this build";
+        case DG_ERR_HIP: return "the HIP runtime reported an error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

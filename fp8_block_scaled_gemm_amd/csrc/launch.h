@@ -1,0 +1,31 @@
+// Internal launchers behind the C ABI (not exported).  Each enqueues its
+// kernels on `stream` and returns the HIP launch status; the C ABI layer has
+// already validated sizes and pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum class Form : int { Dense = 0, Contiguous = 1, Masked = 2 };
+
+struct GemmArgs {
+    const uint8_t* A;     // e4m3 codes, K-contiguous rows
+    const float* sa;      // [rows][K/128]
+    const uint8_t* B;     // [groups][N][K]
+    const float* sb;      // [groups][ceil(N/128)][K/128]
+    uint16_t* D;          // bf16 bits, [rows][N]
+    const int32_t* aux;   // contiguous: group id per row; masked: valid rows per group
+    int64_t rows;         // dense: M; contiguous: M_sum; masked: M_max (rows per slab)
+    int64_t N, K, G;
+};
+
+hipError_t launch_gemm(Form form, const GemmArgs& args, hipStream_t stream);
+
+hipError_t launch_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                                     hipStream_t stream);
+hipError_t launch_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
+                                     hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,126 @@
+/*
+ * dg_fp8.h - C ABI of the MI355X (gfx950) FP8 block-scaled NT GEMM library.
+ *
+ * The operation (DeepGEMM fp8_gemm.cuh, fp8_gemm_kernel: the 128-channel K
+ * block fixed by its static check, the per-block WGMMA partial sum promoted
+ * by the A-row scale times the B-block scale into final_accum, and the
+ * round-to-nearest bf16 epilogue):
+ *
+ *   D[m,n] = bf16( sum_kb (sa[m,kb] * sb[n/128,kb]) * sum_{k in block kb} A[m,k] * B[n,k] )
+ *
+ * with kb = 0 .. K/128-1.  A and B are OCP E4M3FN codes (one byte each, bias
+ * 7, largest finite 448), both K-contiguous ("NT": the layouts that
+ * Gemm::make_2d_tma_a_desc / make_2d_tma_b_desc describe).  D is bf16 stored
+ * as 16-bit patterns, row major, as make_2d_tma_d_desc describes.  Scales are
+ * fp32: sa is one value per row per 128-wide K block, stored row major as
+ * [rows][K/128] (the page's kernel keeps sa M-major; this library fixes the
+ * row-major layout that its quantize helper writes), and sb is one value per
+ * 128x128 block of B, stored [ceil(N/128)][K/128] (the layout the page's
+ * B-scale staging reads).  Column n uses sb row n/128; when N is not a
+ * multiple of 128 the last row covers a partial block.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers to caller-owned, contiguous, row-major
+ *     memory, each aligned to 16 bytes.  The library allocates nothing,
+ *     frees nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream).  No call synchronizes; results are ready when the
+ *     stream reaches them.
+ *   - Arguments are checked on the host before anything is enqueued: sizes
+ *     first, then pointers.  On an error the call returns a nonzero
+ *     dg_status and writes nothing.  A call with no rows to compute (M, M_sum
+ *     or M_max equal to 0) returns DG_OK without looking at its pointers.
+ *   - Rows that a call does not route (M tail, padding rows of the
+ *     contiguous form, rows past masked_m in the masked form) are never
+ *     written.
+ *   - A launch failure reported by the HIP runtime returns DG_ERR_HIP.
+ *   - Calls on different streams may run concurrently; they share nothing.
+ */
+#ifndef DG_FP8_H
+#define DG_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    DG_ERR_SHAPE = 2,       /* a size is out of range (see each call)        */
+    DG_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
+    DG_ERR_UNSUPPORTED = 4, /* valid arguments this build cannot run         */
+    DG_ERR_HIP = 5          /* the HIP runtime reported an error              */
+} dg_status;
+
+/* Dense form.
+ *   A  [M][K]  e4m3 codes          sa [M][K/128]          fp32
+ *   B  [N][K]  e4m3 codes          sb [ceil(N/128)][K/128] fp32
+ *   D  [M][N]  bf16 bits (output)
+ * Sizes: M >= 0 (0 enqueues nothing), N > 0 with N % 8 == 0 (the page's
+ * kernel asserts N % 8), K > 0 with K % 128 == 0 (its static check fixes the
+ * 128-channel K block).  All of M*K, N*K, M*N must be below 2^62. */
+dg_status dg_fp8_gemm_nt(const uint8_t* A, const float* sa,
+                         const uint8_t* B, const float* sb,
+                         uint16_t* D, int64_t M, int64_t N, int64_t K,
+                         void* stream);
+
+/* Contiguous-grouped form (MoE experts with rows sorted by expert).
+ *   A  [M_sum][K]  e4m3         sa [M_sum][K/128]               fp32
+ *   B  [G][N][K]   e4m3         sb [G][ceil(N/128)][K/128]      fp32
+ *   D  [M_sum][N]  bf16 bits    grouped_layout [M_sum] int32 (device)
+ * Row r is computed with B[g], sb[g] for g = grouped_layout[r] when
+ * 0 <= g < G; any other row (padding, id -1) is not written.  Groups are
+ * padded to 128 rows, so M_sum % 128 == 0 and each aligned block of 128 rows
+ * holds at most one group id >= 0; a block that mixes ids has only the rows
+ * of one of them written.  The page's kernel takes the same per-row int
+ * array (grouped_layout) and adds per-group offsets in its scheduler.
+ * Sizes: M_sum >= 0, G >= 1, N and K as for the dense form. */
+dg_status dg_fp8_gemm_grouped_contiguous(const uint8_t* A, const float* sa,
+                                         const uint8_t* B, const float* sb,
+                                         uint16_t* D, const int32_t* grouped_layout,
+                                         int64_t M_sum, int64_t N, int64_t K, int64_t G,
+                                         void* stream);
+
+/* Masked-grouped form (MoE decode: a fixed slab of M_max rows per expert).
+ *   A  [G][M_max][K]  e4m3      sa [G][M_max][K/128]            fp32
+ *   B  [G][N][K]      e4m3      sb [G][ceil(N/128)][K/128]      fp32
+ *   D  [G][M_max][N]  bf16 bits masked_m [G] int32 (device)
+ * Rows r < clamp(masked_m[g], 0, M_max) of slab g are computed with B[g],
+ * sb[g]; the other rows of D are not written, and a group with no valid row
+ * does not read its B.  The page's tensor maps stack the G slabs of A and D
+ * along rows (shape_m * kNumGroups).
+ * Sizes: G >= 1, M_max >= 0, N and K as for the dense form. */
+dg_status dg_fp8_gemm_grouped_masked(const uint8_t* A, const float* sa,
+                                     const uint8_t* B, const float* sb,
+                                     uint16_t* D, const int32_t* masked_m,
+                                     int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                     void* stream);
+
+/* Per-token quantization of activations: x [M][K] fp32 -> q [M][K] e4m3
+ * codes and s [M][K/128] fp32, one scale per row per 128-wide K block.
+ * scale = amax/448 (fp32 IEEE division), q = e4m3 of x/scale (fp32 IEEE
+ * division, round to nearest even, saturated to +-448, sign kept); a block
+ * with amax 0 stores scale 0 and codes 0.  Not on the pages: the recipe is
+ * the workload's, and it fixes the sa layout the GEMM reads.
+ * Sizes: M >= 0, K > 0 with K % 128 == 0. */
+dg_status dg_quantize_fp8_per_token(const float* x, int64_t M, int64_t K,
+                                    uint8_t* q, float* s, void* stream);
+
+/* Per-block quantization of weights: x [N][K] fp32 -> q [N][K] and
+ * s [ceil(N/128)][K/128], one scale per 128x128 block (the last row block is
+ * partial when N % 128 != 0), same rounding as above.  For grouped B call it
+ * on the flattened [G*N][K] when N % 128 == 0, else once per group.
+ * Sizes: N >= 0, K > 0 with K % 128 == 0. */
+dg_status dg_quantize_fp8_per_block(const float* x, int64_t N, int64_t K,
+                                    uint8_t* q, float* s, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* dg_status_string(dg_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_FP8_H */

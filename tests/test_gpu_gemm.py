@@ -1,0 +1,188 @@
+"""GPU parity of the three GEMM forms against the CPU oracle.
+
+Inputs are seeded fp32 draws quantized by the oracle's own quantizer (the GPU
+quantizer is checked separately, bit for bit), so no oracle input comes from
+the HIP path.  Small and medium cases compare every element; the full-size
+workloads compare sampled rows (the oracle computes them one by one) and
+check every unrouted row of D for the untouched 0xFFFF pre-fill."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_gemm_amd as dg
+from fp8_block_scaled_gemm_amd.inputs import (contiguous_case, dense_case, masked_case,
+                                              workload)
+from tests.gpu_util import SENTINEL, assert_close_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_a(orc, x_a: np.ndarray):
+    K = x_a.shape[-1]
+    q, s = orc.quantize_per_token(x_a.reshape(-1, K))
+    return q.reshape(x_a.shape), s.reshape(*x_a.shape[:-1], K // 128)
+
+
+def _quant_b(orc, x_b: np.ndarray):
+    if x_b.ndim == 2:
+        return orc.quantize_per_block(x_b)
+    qs = [orc.quantize_per_block(np.ascontiguousarray(x_b[g])) for g in range(x_b.shape[0])]
+    return np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
+
+
+def _prepared(orc, case):
+    qa, sa = _quant_a(orc, case.x_a.numpy())
+    qb, sb = _quant_b(orc, case.x_b.numpy())
+    return qa, sa, qb, sb
+
+
+def _run(case, qa, sa, qb, sb):
+    A, SA, B, SB = to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
+    if case.form == "dense":
+        D = torch.full((case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
+        dg.dg_fp8_gemm_nt(A, SA, B, SB, D)
+    elif case.form == "contiguous":
+        D = torch.full((case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
+        dg.dg_fp8_gemm_grouped_contiguous(A, SA, B, SB, D, to_dev(case.layout.numpy()))
+    else:
+        D = torch.full((case.G, case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
+        dg.dg_fp8_gemm_grouped_masked(A, SA, B, SB, D, to_dev(case.masked_m.numpy()))
+    torch.cuda.synchronize()
+    return D.cpu().numpy().view(np.uint16)
+
+
+def _oracle_full(orc, case, qa, sa, qb, sb):
+    if case.form == "dense":
+        return orc.gemm_nt(qa, sa, qb, sb)
+    if case.form == "contiguous":
+        return orc.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy())
+    return orc.gemm_grouped_masked(qa, sa, qb, sb, case.masked_m.numpy())
+
+
+def _routed_rows(case) -> np.ndarray:
+    """Flat row indices (into D viewed as [rows][N]) the call must write."""
+    if case.form == "dense":
+        return np.arange(case.M)
+    if case.form == "contiguous":
+        lay = case.layout.numpy()
+        return np.nonzero((lay >= 0) & (lay < case.G))[0]
+    mm = np.clip(case.masked_m.numpy(), 0, case.M)
+    return np.concatenate([g * case.M + np.arange(mm[g]) for g in range(case.G)]).astype(np.int64)
+
+
+def _check_full(orc, case):
+    qa, sa, qb, sb = _prepared(orc, case)
+    got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
+    ref = _oracle_full(orc, case, qa, sa, qb, sb).reshape(-1, case.N)
+    rows = _routed_rows(case)
+    unrouted = np.setdiff1d(np.arange(got.shape[0]), rows)
+    assert (got[unrouted] == 0xFFFF).all(), "an unrouted row of D was written"
+    if rows.size:
+        assert_close_bf16(got[rows], ref[rows], case.name)
+    return got
+
+
+# ------------------------------------------------------------ small/medium
+
+@pytest.mark.parametrize("M,N,K", [
+    (128, 512, 512),      # the smallest named workload
+    (1, 8, 128),          # minimal sizes
+    (300, 712, 1024),     # ragged M and N tails, several tiles
+    (129, 136, 256),      # one row / one 8-column group past a tile
+    (64, 2112 // 4, 384), # N % 128 == 16: partial last scale block
+    (257, 264, 1152),     # odd K-block count
+])
+def test_dense_parity(orc, M, N, K):
+    _check_full(orc, dense_case(M, N, K, seed=M * 7 + N + K, name=f"dense_{M}x{N}x{K}"))
+
+
+def test_dense_parity_scaled_rows(orc):
+    """Rows with very different magnitudes: per-row scales span 2^-20..2^20."""
+    case = dense_case(200, 264, 512, seed=5)
+    case.x_a *= torch.exp2(torch.linspace(-20, 20, 200)).unsqueeze(1)
+    _check_full(orc, case)
+
+
+@pytest.mark.parametrize("sizes", [[100, 0, 260], [128, 1, 255, 3], [0, 0]])
+def test_contiguous_parity(orc, sizes):
+    case = contiguous_case(len(sizes), 264, 512, seed=sum(sizes) + 1, sizes=sizes)
+    if case.M == 0:
+        pytest.skip("no rows")
+    _check_full(orc, case)
+
+
+def test_contiguous_out_of_range_ids_are_padding(orc):
+    case = contiguous_case(3, 136, 256, seed=12, sizes=[200, 50, 128])
+    lay = case.layout.clone()
+    lay[3] = 3          # id == G: not a group
+    lay[130] = 99
+    case.layout = lay
+    _check_full(orc, case)
+
+
+def test_contiguous_all_padding_leaves_d_untouched(orc):
+    case = contiguous_case(2, 64, 256, seed=13, sizes=[0, 0])
+    case.layout = torch.full((256,), -1, dtype=torch.int32)
+    case.M = 256
+    case.x_a = torch.randn(256, 256, generator=torch.Generator().manual_seed(13))
+    got = _check_full(orc, case)
+    assert (got == 0xFFFF).all()
+
+
+@pytest.mark.parametrize("masked", [[0, 200, 37, 129], [200, 200, 200, 200], [1, 0, 128, 2]])
+def test_masked_parity(orc, masked):
+    _check_full(orc, masked_case(4, 200, 136, 384, seed=sum(masked), masked=masked))
+
+
+def test_masked_out_of_range_counts_are_clamped(orc):
+    _check_full(orc, masked_case(3, 64, 24, 256, seed=2, masked=[-5, 1000, 64]))
+
+
+def test_masked_all_zero_leaves_d_untouched(orc):
+    got = _check_full(orc, masked_case(3, 64, 24, 256, seed=3, masked=[0, 0, 0]))
+    assert (got == 0xFFFF).all()
+
+
+def test_zero_scale_block(orc):
+    """A zero block of A (amax 0, scale 0) contributes nothing."""
+    case = dense_case(130, 136, 512, seed=17)
+    case.x_a[:, 128:256] = 0
+    case.x_a[5] = 0
+    _check_full(orc, case)
+
+
+def test_gemm_is_deterministic(orc):
+    case = dense_case(300, 712, 1024, seed=4)
+    qa, sa, qb, sb = _prepared(orc, case)
+    a = _run(case, qa, sa, qb, sb)
+    b = _run(case, qa, sa, qb, sb)
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------- full size
+
+FULL = ["dense_128x512x512", "dense_4096x7168x2048", "dense_64x7168x2048",
+        "dense_128x7168x2048", "dense_4096x24576x1536", "dense_4096x2112x7168",
+        "contiguous_8x4096x7168", "masked_16x256x4096x7168", "masked_16x256x7168x2048"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(orc, name):
+    case = workload(name)
+    qa, sa, qb, sb = _prepared(orc, case)
+    got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
+    routed = _routed_rows(case)
+    unrouted = np.setdiff1d(np.arange(got.shape[0]), routed)
+    assert (got[unrouted] == 0xFFFF).all(), "an unrouted row of D was written"
+    rng = np.random.default_rng(len(name))
+    pick = np.unique(np.concatenate([routed[:2], routed[-2:],
+                                     rng.choice(routed, size=min(12, routed.size), replace=False)]))
+    if case.form == "dense":
+        ref = orc.gemm_nt(qa, sa, qb, sb, rows=pick)
+    elif case.form == "contiguous":
+        ref = orc.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=pick)
+    else:
+        ref = orc.gemm_grouped_masked(qa, sa, qb, sb, case.masked_m.numpy(), rows=pick)
+    assert_close_bf16(got[pick], ref, name)
+    # no routed element may be left at the pre-fill
+    assert not (got[routed] == 0xFFFF).any()
