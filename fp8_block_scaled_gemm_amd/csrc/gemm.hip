@@ -14,29 +14,42 @@
 //   - The MFMA takes B as its first operand and A as its second, so each lane
 //     ends up with one output row and four consecutive output columns: one
 //     scale product per lane and sub-tile, and 8-byte bf16 stores.
-//   - A and B K-slabs (128 bytes per row per K block) are staged in LDS,
-//     double buffered, each 16-byte chunk XOR-swizzled by (row & 7) so the
-//     fragment reads are free of bank conflicts.
+//   - A and B K-slabs (128 bytes per row per K block) go from global memory
+//     straight into LDS (global_load_lds_dwordx4, no register staging),
+//     double buffered.  Each 16-byte chunk of a row sits at chunk ^ (row & 7),
+//     so the 16-lane groups of a fragment read hit distinct banks.
+//   - Workgroups are dispatched round-robin over the 8 XCDs; the tile order
+//     gives each XCD a contiguous range of tiles, grouped a few m-blocks at a
+//     time, so that concurrent tiles on one XCD share A and B slabs in its L2.
 #include "device_common.h"
 #include "launch.h"
 
 namespace dg {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+constexpr int kNumXcds = 8;
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
 struct TileConfig {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+    static constexpr int kWaves = WAVES_M * WAVES_N;
+    static constexpr int kThreads = 64 * kWaves;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // rows / cols per wave
     static constexpr int TM = WM / 16, TN = WN / 16;            // 16x16 sub-tiles per wave
-    static constexpr int kLoadsA = BM * 8 / kThreads;           // 16-byte chunks per thread
-    static constexpr int kLoadsB = BN * 8 / kThreads;
+    static constexpr int kGroupM = GROUP_M_;                    // m-blocks per raster group
+    // one wave-wide direct load fills 1 KiB (8 rows) of a stage
+    static constexpr int kLoadsA = BM / 8 / kWaves;
+    static constexpr int kLoadsB = BN / 8 / kWaves;
+    static constexpr int kStageA = BM * 128, kStageB = BN * 128;
+    // a wave's columns never cross a 128-column scale block
+    static constexpr bool kOneScaleB =
+        (128 % WN == 0) && (BN % 128 == 0 || 128 % BN == 0);
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16x16");
-    static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "uneven staging");
-    static_assert(BM <= kThreads, "one thread per row stages the A scales");
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "uneven staging");
+    static_assert(BM % 64 == 0 && BM / 64 <= kWaves, "one wave per 64 rows stages A scales");
 };
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in LDS.
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in a stage.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
@@ -60,28 +73,69 @@ __device__ __forceinline__ v4f mfma_block(const v8i& b, const v8i& a) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, zero, 0, 0, 0, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave-wide direct load: lane l's bytes from `src` land at
+// dst + size*l in LDS (dst is wave-uniform).
+__device__ __forceinline__ void load_lds_16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds_4(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+}
+
+// Logical tile of workgroup `b` among `tiles`: XCD x (= b % 8) receives the
+// contiguous range [x*per, (x+1)*per); returns -1 for the padding slots.
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+    const int per = (tiles + kNumXcds - 1) / kNumXcds;
+    const int t = (b % kNumXcds) * per + b / kNumXcds;
+    return t < tiles ? t : -1;
+}
+
+// Operands are separate __restrict__ arguments so the compiler knows the
+// scales are never written during the kernel and may use scalar loads.
 template <class T, Form kForm>
-__global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmArgs p, int m_blocks, int n_blocks) {
-    __shared__ __align__(16) uint8_t smA[2][T::BM * 128];
-    __shared__ __align__(16) uint8_t smB[2][T::BN * 128];
-    __shared__ float smSA[2][T::BM];
-    __shared__ int smRowOk[T::BM];
+__global__ __launch_bounds__(T::kThreads) void gemm_kernel(
+    const uint8_t* __restrict__ A_, const float* __restrict__ sa_, const uint8_t* __restrict__ B_,
+    const float* __restrict__ sb_, uint16_t* __restrict__ D_, const int32_t* __restrict__ aux_,
+    int64_t rows_, int64_t N_, int64_t K_, int64_t G_, int m_blocks, int n_blocks) {
+    struct {
+        const uint8_t* __restrict__ A; const float* __restrict__ sa;
+        const uint8_t* __restrict__ B; const float* __restrict__ sb;
+        uint16_t* __restrict__ D; const int32_t* __restrict__ aux;
+        int64_t rows, N, K, G;
+    } p{A_, sa_, B_, sb_, D_, aux_, rows_, N_, K_, G_};
+    __shared__ __align__(1024) uint8_t smA[2][T::kStageA];
+    __shared__ __align__(1024) uint8_t smB[2][T::kStageB];
+    __shared__ __align__(16) float smSA[2][T::BM];
+    __shared__ int smRowOk[kForm == Form::Contiguous ? T::BM : 1];
     __shared__ int smGroup;
 
     const int tid = threadIdx.x;
+    // wave-uniform in a scalar register, so that per-wave addresses (the B
+    // scales) become scalar loads that do not wait on the vector queue
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int64_t K = p.K, N = p.N;
     const int KB = (int)(K >> 7);
     const int NB = (int)((N + 127) >> 7);
 
-    // ---- tile -> (group, m block, n block); m varies fastest so that
-    // consecutive workgroups share one B slab
-    int tile = blockIdx.x;
+    // ---- tile -> (group, m block, n block)
+    const int tiles_per_group = m_blocks * n_blocks;
+    const int groups = kForm == Form::Masked ? (int)p.G : 1;
+    int tile = xcd_tile(blockIdx.x, groups * tiles_per_group);
+    if (tile < 0) return;
     int g = 0;
     if (kForm == Form::Masked) {
-        g = tile / (m_blocks * n_blocks);
-        tile -= g * m_blocks * n_blocks;
+        g = tile / tiles_per_group;
+        tile -= g * tiles_per_group;
     }
-    const int mb = tile % m_blocks, nb = tile / m_blocks;
+    // raster: groups of kGroupM m-blocks, m fastest inside a group
+    const int span = T::kGroupM * n_blocks;
+    const int first_m = (tile / span) * T::kGroupM;
+    const int gm = min(m_blocks - first_m, T::kGroupM);
+    const int in_span = tile % span;
+    const int mb = first_m + in_span % gm, nb = in_span / gm;
     const int m0 = mb * T::BM, n0 = nb * T::BN;
 
     int valid;       // tile rows [0, valid) exist and may be routed
@@ -114,39 +168,39 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmArgs p, int m_blo
     const uint8_t* Bg = p.B + (int64_t)g * N * K;
     const float* sbg = p.sb + (int64_t)g * NB * KB;
 
-    // ---- global -> registers -> LDS staging of one K block
-    v4u ra[T::kLoadsA], rb[T::kLoadsB];
-    float rsa = 0.f;
-#define DG_LOAD_STAGE(kb_)                                                                        \
-    do {                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i) {                                  \
-            const int c = tid + i * T::kThreads, r = min(c >> 3, valid - 1);                      \
-            ra[i] = *reinterpret_cast<const v4u*>(p.A + (arow0 + r) * K + (kb_) * 128 +         \
-                                                    (c & 7) * 16);                                \
-        }                                                                                         \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
-            const int c = tid + i * T::kThreads;                                                  \
-            const int64_t n = min<int64_t>(n0 + (c >> 3), N - 1);                                 \
-            rb[i] = *reinterpret_cast<const v4u*>(Bg + n * K + (kb_) * 128 + (c & 7) * 16);     \
-        }                                                                                         \
-        if (tid < T::BM) rsa = p.sa[(arow0 + min(tid, valid - 1)) * KB + (kb_)];                  \
-    } while (0)
-#define DG_STORE_STAGE(st_)                                                                       \
-    do {                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i) {                                  \
-            const int c = tid + i * T::kThreads;                                                  \
-            *reinterpret_cast<v4u*>(&smA[st_][lds_off(c >> 3, c & 7)]) = ra[i];                 \
-        }                                                                                         \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
-            const int c = tid + i * T::kThreads;                                                  \
-            *reinterpret_cast<v4u*>(&smB[st_][lds_off(c >> 3, c & 7)]) = rb[i];                 \
-        }                                                                                         \
-        if (tid < T::BM) smSA[st_][tid] = rsa;                                                    \
+    // ---- per-lane sources of the direct loads (K block 0); a wave's load i
+    // fills rows [8q, 8q+8) of a stage, q = wave + i * kWaves, and lane l
+    // fetches the logical chunk that belongs at physical chunk l % 8
+    const uint8_t* srcA[T::kLoadsA];
+    const uint8_t* srcB[T::kLoadsB];
+    {
+        const int sub = lane >> 3, pchunk = lane & 7;
+        const int lchunk = pchunk ^ sub;
+#pragma unroll
+        for (int i = 0; i < T::kLoadsA; ++i) {
+            const int row = (wave + i * T::kWaves) * 8 + sub;
+            srcA[i] = p.A + (arow0 + min(row, valid - 1)) * K + lchunk * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < T::kLoadsB; ++i) {
+            const int row = (wave + i * T::kWaves) * 8 + sub;
+            srcB[i] = Bg + min<int64_t>(n0 + row, N - 1) * K + lchunk * 16;
+        }
+    }
+    const float* srcSA = p.sa + (arow0 + min(wave * 64 + lane, valid - 1)) * KB;
+
+#define DG_ISSUE_LOADS(kb_, st_)                                                              \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i)                                \
+            load_lds_16(srcA[i] + (kb_) * 128, &smA[st_][(wave + i * T::kWaves) * 1024]);    \
+        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i)                                \
+            load_lds_16(srcB[i] + (kb_) * 128, &smB[st_][(wave + i * T::kWaves) * 1024]);    \
+        if (wave < T::BM / 64) load_lds_4(srcSA + (kb_), &smSA[st_][wave * 64]);              \
     } while (0)
 
-    const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int wrow = wm * T::WM, wcol = wn * T::WN;
 
     v4f acc[T::TM][T::TN];
 #pragma unroll
@@ -154,50 +208,53 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmArgs p, int m_blo
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    DG_LOAD_STAGE(0);
-    DG_STORE_STAGE(0);
+    DG_ISSUE_LOADS(0, 0);
     __syncthreads();
 
     for (int kb = 0; kb < KB; ++kb) {
         const int st = kb & 1;
-        if (kb + 1 < KB) DG_LOAD_STAGE(kb + 1);
+        if (kb + 1 < KB) DG_ISSUE_LOADS(kb + 1, st ^ 1);
 
+        const uint8_t* sA = smA[st];
+        const uint8_t* sB = smB[st];
         v8i bf[T::TN];
-        float sbv[T::TN];
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            bf[j] = lds_frag(smB[st], wn * T::WN + 16 * j + lr, lg);
-            const int cb = min((n0 + wn * T::WN + 16 * j) >> 7, NB - 1);
-            sbv[j] = sbg[cb * KB + kb];
+        for (int j = 0; j < T::TN; ++j) bf[j] = lds_frag(sB, wcol + 16 * j + lr, lg);
+        float sbv[T::kOneScaleB ? 1 : T::TN];
+        if (T::kOneScaleB) {
+            sbv[0] = sbg[min((n0 + wcol) >> 7, NB - 1) * KB + kb];
+        } else {
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                sbv[j] = sbg[min((n0 + wcol + 16 * j) >> 7, NB - 1) * KB + kb];
         }
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-            const int r = wm * T::WM + 16 * i + lr;
-            const v8i af = lds_frag(smA[st], r, lg);
+            const int r = wrow + 16 * i + lr;
+            const v8i af = lds_frag(sA, r, lg);
             const float s_a = smSA[st][r];
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
                 const v4f part = mfma_block(bf[j], af);
-                const float s = s_a * sbv[j];
+                const float s = s_a * sbv[T::kOneScaleB ? 0 : j];
                 acc[i][j] += s * part;
             }
         }
-
-        if (kb + 1 < KB) DG_STORE_STAGE(st ^ 1);
         __syncthreads();
     }
+#undef DG_ISSUE_LOADS
 
     // ---- epilogue: lane holds row (16i + lr) and columns (16j + 4lg .. +3)
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
-        const int lrow = wm * T::WM + 16 * i + lr;
+        const int lrow = wrow + 16 * i + lr;
         bool ok = lrow < valid;
         if (kForm == Form::Contiguous) ok = ok && smRowOk[lrow];
         if (!ok) continue;
         uint16_t* drow = p.D + (arow0 + lrow) * N;
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-            const int64_t n = n0 + wn * T::WN + 16 * j + 4 * lg;
+            const int64_t n = n0 + wcol + 16 * j + 4 * lg;
             if (n < N) {
                 v2u packed;
                 packed[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
@@ -208,29 +265,31 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmArgs p, int m_blo
     }
 }
 
-#undef DG_LOAD_STAGE
-#undef DG_STORE_STAGE
-
 template <class T, Form kForm>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t m_blocks = (a.rows + T::BM - 1) / T::BM;
     const int64_t n_blocks = (a.N + T::BN - 1) / T::BN;
     const int64_t groups = (kForm == Form::Masked) ? a.G : 1;
-    const int64_t grid = groups * m_blocks * n_blocks;
-    if (grid == 0) return hipSuccess;
+    const int64_t tiles = groups * m_blocks * n_blocks;
+    if (tiles == 0) return hipSuccess;
+    const int64_t grid = (tiles + kNumXcds - 1) / kNumXcds * kNumXcds;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<T, kForm>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
-                       a, (int)m_blocks, (int)n_blocks);
+                       a.A, a.sa, a.B, a.sb, a.D, a.aux, a.rows, a.N, a.K, a.G, (int)m_blocks,
+                       (int)n_blocks);
     return hipGetLastError();
 }
 
-using Tile128 = TileConfig<128, 128, 2, 2>;
+// 256x256 tiles, 8 waves of 128x64 (two per SIMD).
+using TileLarge = TileConfig<256, 256, 2, 4, 4>;
+// 128x256 tiles, 4 waves of 128x64: contiguous groups are padded to 128 rows.
+using TileRows128 = TileConfig<128, 256, 1, 4, 8>;
 
 hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
     switch (form) {
-        case Form::Dense: return launch_tiled<Tile128, Form::Dense>(a, stream);
-        case Form::Contiguous: return launch_tiled<Tile128, Form::Contiguous>(a, stream);
-        case Form::Masked: return launch_tiled<Tile128, Form::Masked>(a, stream);
+        case Form::Dense: return launch_tiled<TileLarge, Form::Dense>(a, stream);
+        case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous>(a, stream);
+        case Form::Masked: return launch_tiled<TileLarge, Form::Masked>(a, stream);
     }
     return hipErrorInvalidValue;
 }
