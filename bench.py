@@ -41,7 +41,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the GEMM, time a plain device copy of this many bytes "
+                         "(the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_reference(nbytes: int, steps: int, warmup: int):
+    """A plain device-to-device copy of known size, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters against bytes actually moved."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": nbytes, "steps": steps, "us_per_copy": round(dt * 1e6, 2),
+                      "GB/s (read+write)": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
 def algorithmic(case):
@@ -194,6 +216,10 @@ def main():
               "the multi-GPU sharding of this path is a design note, not a measured path",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_bytes:
+        copy_reference(args.copy_bytes, args.steps, args.warmup)
+        return
 
     import torch
     import fp8_block_scaled_gemm_amd as dg
