@@ -11,6 +11,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));  // 16-byte global/LDS chunk
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 bit pattern, round to nearest, ties to even (the rounding of
 // the bf16 epilogue in DeepGEMM fp8_gemm.cuh).  NaN stays a quiet NaN;

@@ -6,23 +6,33 @@
 // F += (sa[m,kb] * sb[n/128,kb]) * P; the epilogue rounds F to bf16 (nearest
 // even) and stores the rows the call routes.
 //
-// How it maps to CDNA4:
+// How it maps to CDNA4 (gfx950):
 //   - One v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3, C = 0) covers a whole
 //     128-wide K block of a 16x16 sub-tile, so its result *is* the block
 //     partial P and goes straight into the promotion FMA; no second set of
 //     accumulators is kept.
 //   - The MFMA takes B as its first operand and A as its second, so each lane
-//     ends up with one output row and four consecutive output columns: one
-//     scale product per lane and sub-tile, and 8-byte bf16 stores.
-//   - A and B K-slabs (128 bytes per row per K block) go from global memory
-//     straight into LDS (global_load_lds_dwordx4, no register staging),
-//     double buffered.  Each 16-byte chunk of a row sits at chunk ^ (row & 7),
-//     so the 16-lane groups of a fragment read hit distinct banks.
+//     owns one output row and four consecutive output columns: one scale
+//     product per lane and sub-tile.
+//   - LDS bandwidth (about 128 bytes per clock per CU for these reads) is the
+//     scarce resource, so only A goes through LDS: its K-slab (128 bytes per
+//     row per K block) is loaded straight from memory into a double-buffered
+//     LDS stage with bounds-checked buffer loads (rows past the valid rows
+//     read as zero and touch no memory).  Each 16-byte chunk of a row sits at
+//     chunk ^ (row & 7), so the 16-lane groups of a fragment read hit distinct
+//     banks.  B fragments are read by each wave straight into registers one K
+//     block ahead; the two waves that share B columns sit on one SIMD and
+//     share them through the L1 cache.
+//   - The output tile is staged through LDS in bf16 and written back in full
+//     16-byte chunks per lane, whole row segments per store instruction
+//     (scattered 8-byte fragment stores reach half the write bandwidth).
 //   - Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //     gives each XCD a contiguous range of tiles, grouped a few m-blocks at a
 //     time, so that concurrent tiles on one XCD share A and B slabs in its L2.
 #include "device_common.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace dg {
 
@@ -40,30 +50,72 @@ struct TileConfig {
     // one wave-wide direct load fills 1 KiB (8 rows) of a stage
     static constexpr int kLoadsA = BM / 8 / kWaves;
     static constexpr int kLoadsB = BN / 8 / kWaves;
-    static constexpr int kStageA = BM * 128, kStageB = BN * 128;
-    // a wave's columns never cross a 128-column scale block
-    static constexpr bool kOneScaleB =
-        (128 % WN == 0) && (BN % 128 == 0 || 128 % BN == 0);
+    static constexpr int kStageA = BM * 128;
+    static constexpr int kStageB = BN * 128;
+    // the bf16 output tile reuses the stage memory on its way out
+    static constexpr int kSmem = (2 * (kStageA + kStageB) > BM * BN * 2) ? 2 * (kStageA + kStageB)
+                                                                         : BM * BN * 2;
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16x16");
-    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "uneven staging");
-    static_assert(BM % 64 == 0 && BM / 64 <= kWaves, "one wave per 64 rows stages A scales");
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "uneven slab staging");
+    static_assert(BN % 128 == 0 && 128 % WN == 0, "a wave's columns share one column-scale block");
+    static_assert(BM % 64 == 0 && kWaves % (BM / 64) == 0, "waves stage the A scales 64 rows each");
 };
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` in a stage.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * 128 + ((chunk ^ (row & 7)) << 4);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_ptr_t)p));
 }
 
-// MFMA operand: lane (lr, lg) supplies 32 bytes of row `row`, chunks 2*lg and
-// 2*lg+1.  A and B fragments use the same K assignment, so the dot product
-// pairs matching K indices whatever order the instruction walks them in.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int lg) {
-    const v4u lo = *reinterpret_cast<const v4u*>(base + lds_off(row, 2 * lg));
-    const v4u hi = *reinterpret_cast<const v4u*>(base + lds_off(row, 2 * lg + 1));
-    v8i r;
-    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
-    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+// Raw buffer resource (gfx9 V#): `bytes` readable from `base`, stride 0.
+// Loads at offsets past `bytes` return zero and touch no memory.
+__device__ __forceinline__ v4u buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4u r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xffffu;
+    r[2] = bytes;
+    r[3] = 0x00020000u;
     return r;
+}
+
+// One wave-wide direct load: lane l's bytes at buffer offset `off` land at
+// dst + size*l in LDS (dst is wave-uniform, passed in M0).  Written as inline
+// assembly on purpose: the compiler then does not track these LDS writes and
+// cannot put a wait for the stage being filled in front of reads of the
+// other stage (its alias tracking for such loads depends on control flow).
+// The kernel orders them itself with explicit vmcnt waits before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void load_lds_16(const v4u& rsrc, uint32_t off, void* dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds_4(const v4u& rsrc, uint32_t off, void* dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// The same with lgkmcnt = 0: every LDS access this wave issued has completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses, but
+// (unlike __syncthreads) waits for nothing: the kernel has already waited for
+// exactly the loads the barrier publishes.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ v4f mfma_block(const v8i& b, const v8i& a) {
@@ -73,134 +125,177 @@ __device__ __forceinline__ v4f mfma_block(const v8i& b, const v8i& a) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, zero, 0, 0, 0, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// One wave-wide direct load: lane l's bytes from `src` land at
-// dst + size*l in LDS (dst is wave-uniform).
-__device__ __forceinline__ void load_lds_16(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void load_lds_4(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+__device__ __forceinline__ v8i join(const v4u& lo, const v4u& hi) {
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 // Logical tile of workgroup `b` among `tiles`: XCD x (= b % 8) receives the
-// contiguous range [x*per, (x+1)*per); returns -1 for the padding slots.
+// contiguous range [x*per, (x+1)*per); -1 for the padding slots.
 __device__ __forceinline__ int xcd_tile(int b, int tiles) {
     const int per = (tiles + kNumXcds - 1) / kNumXcds;
     const int t = (b % kNumXcds) * per + b / kNumXcds;
     return t < tiles ? t : -1;
 }
 
-// Operands are separate __restrict__ arguments so the compiler knows the
-// scales are never written during the kernel and may use scalar loads.
+// Where one output tile lives.  Every field is wave-uniform.
+struct TileInfo {
+    int g;              // group (0 for dense)
+    int m0, n0;         // first row within the group's row space, first column
+    int valid;          // tile rows [0, valid) exist and may be routed
+    int64_t arow0;      // A / sa / D row of tile row 0
+    uint64_t ok0, ok1;  // contiguous form: routed-row masks, tile rows 0-63 / 64-127
+};
+
+// Decode workgroup `b`'s tile; false when it is a padding slot or the tile
+// has no routed row (masked rows past masked_m, contiguous blocks of
+// padding).  Contiguous: the block's group is the largest id in [0, G) among
+// its rows (the layout puts one id per 128-row block), and only rows carrying
+// that id are routed; every wave computes this from the layout itself.
 template <class T, Form kForm>
-__global__ __launch_bounds__(T::kThreads) void gemm_kernel(
-    const uint8_t* __restrict__ A_, const float* __restrict__ sa_, const uint8_t* __restrict__ B_,
-    const float* __restrict__ sb_, uint16_t* __restrict__ D_, const int32_t* __restrict__ aux_,
-    int64_t rows_, int64_t N_, int64_t K_, int64_t G_, int m_blocks, int n_blocks) {
-    struct {
-        const uint8_t* __restrict__ A; const float* __restrict__ sa;
-        const uint8_t* __restrict__ B; const float* __restrict__ sb;
-        uint16_t* __restrict__ D; const int32_t* __restrict__ aux;
-        int64_t rows, N, K, G;
-    } p{A_, sa_, B_, sb_, D_, aux_, rows_, N_, K_, G_};
-    __shared__ __align__(1024) uint8_t smA[2][T::kStageA];
-    __shared__ __align__(1024) uint8_t smB[2][T::kStageB];
-    __shared__ __align__(16) float smSA[2][T::BM];
-    __shared__ int smRowOk[kForm == Form::Contiguous ? T::BM : 1];
-    __shared__ int smGroup;
-
-    const int tid = threadIdx.x;
-    // wave-uniform in a scalar register, so that per-wave addresses (the B
-    // scales) become scalar loads that do not wait on the vector queue
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int64_t K = p.K, N = p.N;
-    const int KB = (int)(K >> 7);
-    const int NB = (int)((N + 127) >> 7);
-
-    // ---- tile -> (group, m block, n block)
+__device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, int64_t rows,
+                                            int64_t G, const int32_t* __restrict__ aux,
+                                            int lane, TileInfo& ti) {
     const int tiles_per_group = m_blocks * n_blocks;
-    const int groups = kForm == Form::Masked ? (int)p.G : 1;
-    int tile = xcd_tile(blockIdx.x, groups * tiles_per_group);
-    if (tile < 0) return;
-    int g = 0;
+    const int groups = kForm == Form::Masked ? (int)G : 1;
+    int tile = xcd_tile(b, groups * tiles_per_group);
+    if (tile < 0) return false;
+    ti.g = 0;
     if (kForm == Form::Masked) {
-        g = tile / tiles_per_group;
-        tile -= g * tiles_per_group;
+        ti.g = tile / tiles_per_group;
+        tile -= ti.g * tiles_per_group;
     }
     // raster: groups of kGroupM m-blocks, m fastest inside a group
     const int span = T::kGroupM * n_blocks;
     const int first_m = (tile / span) * T::kGroupM;
     const int gm = min(m_blocks - first_m, T::kGroupM);
     const int in_span = tile % span;
-    const int mb = first_m + in_span % gm, nb = in_span / gm;
-    const int m0 = mb * T::BM, n0 = nb * T::BN;
-
-    int valid;       // tile rows [0, valid) exist and may be routed
-    int64_t arow0;   // A / sa / D row of tile row 0
+    ti.m0 = (first_m + in_span % gm) * T::BM;
+    ti.n0 = (in_span / gm) * T::BN;
+    ti.ok0 = ti.ok1 = 0;
     if (kForm == Form::Dense) {
-        valid = (int)min<int64_t>(T::BM, p.rows - m0);
-        arow0 = m0;
+        ti.valid = (int)min<int64_t>(T::BM, rows - ti.m0);
+        ti.arow0 = ti.m0;
     } else if (kForm == Form::Masked) {
-        const int64_t vm = min<int64_t>(max(p.aux[g], 0), p.rows);
-        if (m0 >= vm) return;  // whole tile past masked_m: uniform exit
-        valid = (int)min<int64_t>(T::BM, vm - m0);
-        arow0 = (int64_t)g * p.rows + m0;
+        const int64_t vm = min<int64_t>(max(aux[ti.g], 0), rows);
+        if (ti.m0 >= vm) return false;
+        ti.valid = (int)min<int64_t>(T::BM, vm - ti.m0);
+        ti.arow0 = (int64_t)ti.g * rows + ti.m0;
     } else {
-        // contiguous: the tile's group is the id of its routed rows (ids
-        // outside [0, G) are padding); one id per 128-row block
-        valid = T::BM;
-        arow0 = m0;
-        if (tid == 0) smGroup = -1;
-        __syncthreads();
-        int id = -1;
-        if (tid < T::BM) {
-            id = p.aux[m0 + tid];
-            if (id >= 0 && id < p.G) atomicMax(&smGroup, id);
-        }
-        __syncthreads();
-        g = smGroup;
-        if (g < 0) return;  // all padding: uniform exit
-        if (tid < T::BM) smRowOk[tid] = (id == g);
-    }
-    const uint8_t* Bg = p.B + (int64_t)g * N * K;
-    const float* sbg = p.sb + (int64_t)g * NB * KB;
-
-    // ---- per-lane sources of the direct loads (K block 0); a wave's load i
-    // fills rows [8q, 8q+8) of a stage, q = wave + i * kWaves, and lane l
-    // fetches the logical chunk that belongs at physical chunk l % 8
-    const uint8_t* srcA[T::kLoadsA];
-    const uint8_t* srcB[T::kLoadsB];
-    {
-        const int sub = lane >> 3, pchunk = lane & 7;
-        const int lchunk = pchunk ^ sub;
+        static_assert(kForm != Form::Contiguous || T::BM == 128, "one group per 128-row block");
+        const int id0 = aux[ti.m0 + lane], id1 = aux[ti.m0 + 64 + lane];
+        int gid = max((id0 >= 0 && id0 < G) ? id0 : -1, (id1 >= 0 && id1 < G) ? id1 : -1);
 #pragma unroll
-        for (int i = 0; i < T::kLoadsA; ++i) {
-            const int row = (wave + i * T::kWaves) * 8 + sub;
-            srcA[i] = p.A + (arow0 + min(row, valid - 1)) * K + lchunk * 16;
-        }
-#pragma unroll
-        for (int i = 0; i < T::kLoadsB; ++i) {
-            const int row = (wave + i * T::kWaves) * 8 + sub;
-            srcB[i] = Bg + min<int64_t>(n0 + row, N - 1) * K + lchunk * 16;
-        }
+        for (int d = 32; d >= 1; d >>= 1) gid = max(gid, __shfl_xor(gid, d, 64));
+        gid = __builtin_amdgcn_readfirstlane(gid);
+        if (gid < 0) return false;
+        ti.g = gid;
+        ti.ok0 = __ballot(id0 == gid);
+        ti.ok1 = __ballot(id1 == gid);
+        ti.valid = T::BM;
+        ti.arow0 = ti.m0;
     }
-    const float* srcSA = p.sa + (arow0 + min(wave * 64 + lane, valid - 1)) * KB;
+    return true;
+}
 
-#define DG_ISSUE_LOADS(kb_, st_)                                                              \
-    do {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i)                                \
-            load_lds_16(srcA[i] + (kb_) * 128, &smA[st_][(wave + i * T::kWaves) * 1024]);    \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i)                                \
-            load_lds_16(srcB[i] + (kb_) * 128, &smB[st_][(wave + i * T::kWaves) * 1024]);    \
-        if (wave < T::BM / 64) load_lds_4(srcSA + (kb_), &smSA[st_][wave * 64]);              \
-    } while (0)
+// Operands are separate __restrict__ arguments so the compiler knows they
+// are never written during the kernel.
+//
+// Pipeline (one K block = one step, one barrier per step): during step kb
+// each wave
+//   - loads its share of the A slab of block kb+1 (with its row scales and
+//     the tile's column scales) into A stage (kb+1)&1, and of the B slab of
+//     block kb+2 into B stage kb&1, straight from memory into LDS;
+//   - multiplies block kb: B fragments from registers, A fragments streamed
+//     from A stage kb&1 one row of sub-tiles at a time;
+//   - reads its B fragments of block kb+1 (published by the previous
+//     barrier) into a second register set.
+// So no barrier is followed by a burst of B fragment reads that would leave
+// the matrix cores idle; only the first A fragment of a step waits for LDS.
+template <class T, Form kForm>
+__global__ __launch_bounds__(T::kThreads) void gemm_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
+    const float* __restrict__ sb, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
+    int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks, int n_blocks) {
+    // Two A stages then two B stages (after the K loop: the bf16 output tile);
+    // two stages of A row scales and of column-block scales.
+    __shared__ __align__(1024) uint8_t smem[T::kSmem];
+    __shared__ __align__(16) float smSA[2][T::BM];
+    __shared__ __align__(16) float smSB[2][64];
 
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int KB = (int)(K >> 7);
+    const int NB = (int)((N + 127) >> 7);
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
     const int wrow = wm * T::WM, wcol = wn * T::WN;
+
+    TileInfo ti;
+    if (!decode_tile<T, kForm>(blockIdx.x, m_blocks, n_blocks, rows, G, aux, lane, ti)) return;
+
+    uint8_t* const smA = smem;
+    uint8_t* const smB = smem + 2 * T::kStageA;
+
+    // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
+    // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
+    // belongs at physical chunk l % 8.  Each load's buffer starts at its first
+    // row and ends at the tile's last valid row (A) or column (B); blocks past
+    // the last one get an empty buffer, so their loads move no data but still
+    // count towards the wave's vmcnt like every other step's.
+    const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
+    const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
+    const int sa_rows = (wave % (T::BM / 64)) * 64;
+    const uint32_t offSA = (uint32_t)(sa_rows + lane) * (uint32_t)KB * 4;
+    const uint32_t offSB = (uint32_t)lane * (uint32_t)KB * 4;
+    const int nb0 = ti.n0 >> 7;
+    const int vn = (int)min<int64_t>(T::BN, N - ti.n0);
+    const int vnb = min(T::BN / 128, NB - nb0);  // column-scale blocks the tile touches
+    const uint8_t* tileA = A + ti.arow0 * K;
+    const float* tileSA = sa + ti.arow0 * KB;
+    const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
+    const float* tileSB = sb + ((int64_t)ti.g * NB + nb0) * KB;
+#define DG_ISSUE_A(kb_, st_)                                                                      \
+    do {                                                                                          \
+        const bool live_ = (kb_) < KB;                                                            \
+        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i) {                                  \
+            const int r0 = i * T::kWaves * 8;                                                     \
+            load_lds_16(buffer_rsrc(tileA + (int64_t)r0 * K + (kb_) * 128,                        \
+                                    live_ ? (uint32_t)max(ti.valid - r0, 0) * (uint32_t)K : 0u),  \
+                        offRow, smA + (st_) * T::kStageA + (wave + i * T::kWaves) * 1024);        \
+        }                                                                                         \
+        load_lds_4(buffer_rsrc(tileSA + (kb_), live_ ? (uint32_t)ti.valid * KB * 4 : 0u), offSA,  \
+                   &smSA[st_][sa_rows]);                                                          \
+        load_lds_4(buffer_rsrc(tileSB + (kb_), live_ ? (uint32_t)vnb * KB * 4 - (kb_) * 4 : 0u),   \
+                   offSB, &smSB[st_][0]);                                                         \
+    } while (0)
+#define DG_ISSUE_B(kb_, st_)                                                                      \
+    do {                                                                                          \
+        const bool live_ = (kb_) < KB;                                                            \
+        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
+            const int r0 = i * T::kWaves * 8;                                                     \
+            load_lds_16(buffer_rsrc(tileB + (int64_t)r0 * K + (kb_) * 128,                        \
+                                    live_ ? (uint32_t)max(vn - r0, 0) * (uint32_t)K : 0u),        \
+                        offRow, smB + (st_) * T::kStageB + (wave + i * T::kWaves) * 1024);        \
+        }                                                                                         \
+    } while (0)
+
+    // ---- fragment reads.  Row r of a stage has (r & 7) == (lr & 7) for every
+    // row a lane reads, so the swizzled chunk offsets are per-lane constants
+    // and sub-tile i (or j) only adds 16 rows (an immediate).
+    const int chunk_lo = ((2 * lg) ^ (lr & 7)) << 4, chunk_hi = ((2 * lg + 1) ^ (lr & 7)) << 4;
+    const int fragA = (wrow + lr) * 128, fragB = (wcol + lr) * 128;
+    const int srow = wrow + lr;
+    const int sblk = wcol >> 7;  // the wave's column-scale block within the tile
+#define DG_FRAG(base_, off_)                                                                      \
+    join(*reinterpret_cast<const v4u*>((base_) + (off_) + chunk_lo),                             \
+         *reinterpret_cast<const v4u*>((base_) + (off_) + chunk_hi))
+#define DG_LOAD_BF(bf_, st_)                                                                      \
+    do {                                                                                          \
+        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                         \
+            bf_[j] = DG_FRAG(smB + (st_) * T::kStageB, fragB + j * 16 * 128);                     \
+    } while (0)
 
     v4f acc[T::TM][T::TN];
 #pragma unroll
@@ -208,60 +303,93 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    DG_ISSUE_LOADS(0, 0);
-    __syncthreads();
+    // rows [i0_, i1_) of the wave tile for K block on stage st_
+#define DG_ROWS(bf_use, st_, i0_, i1_)                                                            \
+    do {                                                                                          \
+        const float s_b_ = smSB[st_][sblk];                                                       \
+        _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
+            const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * 16 * 128);             \
+            const float s_ = smSA[st_][srow + 16 * i] * s_b_;                                     \
+            _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
+                acc[i][j] += s_ * mfma_block(bf_use[j], af_);                                     \
+        }                                                                                         \
+    } while (0)
 
-    for (int kb = 0; kb < KB; ++kb) {
-        const int st = kb & 1;
-        if (kb + 1 < KB) DG_ISSUE_LOADS(kb + 1, st ^ 1);
+    // One K block kb_ on stages st_ (= kb_ & 1).  The B fragments of block
+    // kb_+1 are read in the middle of the step, between the two halves of
+    // the rows; the step ends by waiting for this wave's slab loads (A of
+    // kb_+1, B of kb_+2) and for its LDS reads, then the barrier publishes
+    // the new slabs and frees the ones this step read.
+#define DG_STEP(bf_use, bf_next, kb_, st_)                                                        \
+    do {                                                                                          \
+        DG_ISSUE_A((kb_) + 1, (st_) ^ 1);                                                         \
+        DG_ISSUE_B((kb_) + 2, (st_));                                                             \
+        DG_ROWS(bf_use, st_, 0, T::TM / 2);                                                       \
+        DG_LOAD_BF(bf_next, (st_) ^ 1);                                                           \
+        DG_ROWS(bf_use, st_, T::TM / 2, T::TM);                                                   \
+        wait_vmcnt_lgkm0<0>();                                                                    \
+        lds_barrier();                                                                            \
+    } while (0)
 
-        const uint8_t* sA = smA[st];
-        const uint8_t* sB = smB[st];
-        v8i bf[T::TN];
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) bf[j] = lds_frag(sB, wcol + 16 * j + lr, lg);
-        float sbv[T::kOneScaleB ? 1 : T::TN];
-        if (T::kOneScaleB) {
-            sbv[0] = sbg[min((n0 + wcol) >> 7, NB - 1) * KB + kb];
-        } else {
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                sbv[j] = sbg[min((n0 + wcol + 16 * j) >> 7, NB - 1) * KB + kb];
-        }
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            const int r = wrow + 16 * i + lr;
-            const v8i af = lds_frag(sA, r, lg);
-            const float s_a = smSA[st][r];
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const v4f part = mfma_block(bf[j], af);
-                const float s = s_a * sbv[T::kOneScaleB ? 0 : j];
-                acc[i][j] += s * part;
-            }
-        }
-        __syncthreads();
+    v8i bf0[T::TN], bf1[T::TN];
+    DG_ISSUE_A(0, 0);
+    DG_ISSUE_B(0, 0);
+    DG_ISSUE_B(1, 1);
+    wait_vmcnt<0>();
+    lds_barrier();
+    DG_LOAD_BF(bf0, 0);
+    wait_vmcnt_lgkm0<0>();  // B stage 0 is read before step 0 refills it
+    lds_barrier();
+
+    for (int kb = 0; kb < KB; kb += 2) {
+        DG_STEP(bf0, bf1, kb, 0);
+        if (kb + 1 < KB) DG_STEP(bf1, bf0, kb + 1, 1);
     }
-#undef DG_ISSUE_LOADS
+#undef DG_STEP
+#undef DG_ROWS
+#undef DG_LOAD_BF
+#undef DG_FRAG
+#undef DG_ISSUE_B
+#undef DG_ISSUE_A
 
-    // ---- epilogue: lane holds row (16i + lr) and columns (16j + 4lg .. +3)
+    // ---- epilogue.  Lane holds row (16i + lr), columns (16j + 4lg .. +3) of
+    // its wave tile.  Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage
+    // the whole tile in LDS, then write it back in full 16-byte chunks.  In
+    // LDS, 16-byte chunk c of row r sits at c ^ (r & 15): the 16 rows a
+    // fragment store touches land in distinct banks.
+    constexpr int kRowBytes = T::BN * 2;
+    constexpr int kChunks = kRowBytes / 16;
+    static_assert(kChunks % 16 == 0 && 64 % kChunks == 0, "row chunking");
+    wait_vmcnt<0>();  // the empty loads of the last steps have retired
+    lds_barrier();
+    uint8_t* const sD = smem;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
-        const int lrow = wrow + 16 * i + lr;
-        bool ok = lrow < valid;
-        if (kForm == Form::Contiguous) ok = ok && smRowOk[lrow];
-        if (!ok) continue;
-        uint16_t* drow = p.D + (arow0 + lrow) * N;
+        const int row = wrow + 16 * i + lr;
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-            const int64_t n = n0 + wcol + 16 * j + 4 * lg;
-            if (n < N) {
-                v2u packed;
-                packed[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-                packed[1] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-                *reinterpret_cast<v2u*>(drow + n) = packed;
-            }
+            const int col = wcol + 16 * j + 4 * lg;
+            const v2f lo = {acc[i][j][0], acc[i][j][1]};
+            const v2f hi = {acc[i][j][2], acc[i][j][3]};
+            v2u packed;
+            packed[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2bf));
+            packed[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2bf));
+            *reinterpret_cast<v2u*>(sD + row * kRowBytes + (((col >> 3) ^ (row & 15)) << 4) +
+                                    ((col >> 2) & 1) * 8) = packed;
         }
+    }
+    __syncthreads();
+    constexpr int kRowsPerPass = 64 / kChunks;  // rows one wave-wide access covers
+    const int prow = lane / kChunks, pchunk = lane % kChunks;
+    const int64_t col = ti.n0 + pchunk * 8;
+#pragma unroll 4
+    for (int r = wave * kRowsPerPass; r < T::BM; r += T::kWaves * kRowsPerPass) {
+        const int row = r + prow;
+        bool ok = row < ti.valid && col < N;
+        if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
+        const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes +
+                                                    ((pchunk ^ (row & 15)) << 4));
+        if (ok) *reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col) = v;
     }
 }
 
@@ -274,6 +402,8 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     if (tiles == 0) return hipSuccess;
     const int64_t grid = (tiles + kNumXcds - 1) / kNumXcds * kNumXcds;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    // per-lane 32-bit offsets: a tile's rows of K bytes, its A scales
+    if ((int64_t)std::max(T::BM, T::BN) * a.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<T, kForm>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
                        a.A, a.sa, a.B, a.sb, a.D, a.aux, a.rows, a.N, a.K, a.G, (int)m_blocks,
                        (int)n_blocks);
