@@ -38,7 +38,18 @@ namespace dg {
 
 constexpr int kNumXcds = 8;
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
+#ifndef DG_PF_DENSE
+#define DG_PF_DENSE 0
+#endif
+#ifndef DG_PF_CONTIG
+#define DG_PF_CONTIG 0
+#endif
+#ifndef DG_PF_MASKED
+#define DG_PF_MASKED 0
+#endif
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_, bool ROW_SKIP_,
+          int PREFETCH_>
 struct TileConfig {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -47,6 +58,15 @@ struct TileConfig {
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // rows / cols per wave
     static constexpr int TM = WM / 16, TN = WN / 16;            // 16x16 sub-tiles per wave
     static constexpr int kGroupM = GROUP_M_;                    // m-blocks per raster group
+    // skip the MFMAs of sub-tile rows past the tile's valid rows, a quarter
+    // of the wave tile at a time (worth it where tiles are often partial)
+    static constexpr bool kRowSkip = ROW_SKIP_;
+    // Besides the slabs of the next blocks (landing in LDS), each step asks
+    // for the cache lines of the slabs kPrefetch blocks further ahead, so
+    // that they are on chip when their slab load is issued (0: off).  Streams
+    // that come from HBM need more bytes in flight than two LDS stages hold.
+    static constexpr int kPrefetch = PREFETCH_;
+    static constexpr int kPrefetchOps = PREFETCH_ > 0 ? 2 : 0;
     // one wave-wide direct load fills 1 KiB (8 rows) of a stage
     static constexpr int kLoadsA = BM / 8 / kWaves;
     static constexpr int kLoadsB = BN / 8 / kWaves;
@@ -59,6 +79,7 @@ struct TileConfig {
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "uneven slab staging");
     static_assert(BN % 128 == 0 && 128 % WN == 0, "a wave's columns share one column-scale block");
     static_assert(BM % 64 == 0 && kWaves % (BM / 64) == 0, "waves stage the A scales 64 rows each");
+    static_assert(BM <= 32 * kWaves && BN <= 32 * kWaves, "a wave's prefetch covers 32 rows of a slab");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -222,6 +243,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     __shared__ __align__(1024) uint8_t smem[T::kSmem];
     __shared__ __align__(16) float smSA[2][T::BM];
     __shared__ __align__(16) float smSB[2][64];
+    __shared__ __align__(16) float smPF[64];  // sink of the prefetch loads, never read
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -230,7 +252,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const int NB = (int)((N + 127) >> 7);
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
-    const int wrow = wm * T::WM, wcol = wn * T::WN;
+    const int wcol = wn * T::WN;
 
     TileInfo ti;
     if (!decode_tile<T, kForm>(blockIdx.x, m_blocks, n_blocks, rows, G, aux, lane, ti)) return;
@@ -281,12 +303,34 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         }                                                                                         \
     } while (0)
 
-    // ---- fragment reads.  Row r of a stage has (r & 7) == (lr & 7) for every
-    // row a lane reads, so the swizzled chunk offsets are per-lane constants
-    // and sub-tile i (or j) only adds 16 rows (an immediate).
+    // Prefetch: wave w asks for one 4-byte word in each of the 128-byte lines
+    // of rows [32w, 32w + 32) of the A slab and of the B slab (lanes 32-63
+    // point past every buffer and move nothing).
+    const uint32_t offPF = lane < 32 ? (uint32_t)(32 * wave + lane) * (uint32_t)K : 0xffffff00u;
+#define DG_PREFETCH(kba_, kbb_)                                                                   \
+    do {                                                                                          \
+        if (T::kPrefetch > 0) {                                                                   \
+            load_lds_4(buffer_rsrc(tileA + (kba_) * 128,                                          \
+                                   (kba_) < KB ? (uint32_t)ti.valid * (uint32_t)K : 0u),          \
+                       offPF, smPF);                                                              \
+            load_lds_4(buffer_rsrc(tileB + (kbb_) * 128,                                          \
+                                   (kbb_) < KB ? (uint32_t)vn * (uint32_t)K : 0u),                \
+                       offPF, smPF);                                                              \
+        }                                                                                         \
+    } while (0)
+
+    // ---- fragment reads.  Sub-tile row i of wave row wm covers tile rows
+    // [16 (WAVES_M i + wm), +16): the wave rows interleave in 16-row steps, so
+    // a partial tile (a masked group's last rows, a ragged M) leaves work on
+    // every wave.  Row r of a stage has (r & 7) == (lr & 7) for every row a
+    // lane reads, so the swizzled chunk offsets are per-lane constants and
+    // sub-tile i (or j) only adds a multiple of 16 rows (an immediate).
+    constexpr int kRowStep = 16 * T::WAVES_M;
     const int chunk_lo = ((2 * lg) ^ (lr & 7)) << 4, chunk_hi = ((2 * lg + 1) ^ (lr & 7)) << 4;
-    const int fragA = (wrow + lr) * 128, fragB = (wcol + lr) * 128;
-    const int srow = wrow + lr;
+    const int fragA = (16 * wm + lr) * 128, fragB = (wcol + lr) * 128;
+    const int srow = 16 * wm + lr;
+    // sub-tile rows of this wave that hold valid rows; the others are skipped
+    const int vsub = (ti.valid - 16 * wm + kRowStep - 1) / kRowStep;
     const int sblk = wcol >> 7;  // the wave's column-scale block within the tile
 #define DG_FRAG(base_, off_)                                                                      \
     join(*reinterpret_cast<const v4u*>((base_) + (off_) + chunk_lo),                             \
@@ -303,16 +347,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // rows [i0_, i1_) of the wave tile for K block on stage st_
+    // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_
 #define DG_ROWS(bf_use, st_, i0_, i1_)                                                            \
     do {                                                                                          \
         const float s_b_ = smSB[st_][sblk];                                                       \
         _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
-            const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * 16 * 128);             \
-            const float s_ = smSA[st_][srow + 16 * i] * s_b_;                                     \
+            const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);       \
+            const float s_ = smSA[st_][srow + kRowStep * i] * s_b_;                               \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
                 acc[i][j] += s_ * mfma_block(bf_use[j], af_);                                     \
         }                                                                                         \
+    } while (0)
+    // With kRowSkip, a quarter of the sub-tile rows runs only when it holds
+    // valid rows: one uniform branch per quarter.
+#define DG_QUARTER(bf_use, st_, q_)                                                               \
+    do {                                                                                          \
+        if (!T::kRowSkip || (q_) == 0 || vsub > (q_) * (T::TM / 4))                               \
+            DG_ROWS(bf_use, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4));                  \
     } while (0)
 
     // One K block kb_ on stages st_ (= kb_ & 1).  The B fragments of block
@@ -324,10 +375,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     do {                                                                                          \
         DG_ISSUE_A((kb_) + 1, (st_) ^ 1);                                                         \
         DG_ISSUE_B((kb_) + 2, (st_));                                                             \
-        DG_ROWS(bf_use, st_, 0, T::TM / 2);                                                       \
+        DG_PREFETCH((kb_) + 1 + T::kPrefetch, (kb_) + 2 + T::kPrefetch);                          \
+        DG_QUARTER(bf_use, st_, 0);                                                               \
+        DG_QUARTER(bf_use, st_, 1);                                                               \
         DG_LOAD_BF(bf_next, (st_) ^ 1);                                                           \
-        DG_ROWS(bf_use, st_, T::TM / 2, T::TM);                                                   \
-        wait_vmcnt_lgkm0<0>();                                                                    \
+        DG_QUARTER(bf_use, st_, 2);                                                               \
+        DG_QUARTER(bf_use, st_, 3);                                                               \
+        wait_vmcnt_lgkm0<T::kPrefetchOps>();                                                      \
         lds_barrier();                                                                            \
     } while (0)
 
@@ -346,14 +400,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         if (kb + 1 < KB) DG_STEP(bf1, bf0, kb + 1, 1);
     }
 #undef DG_STEP
+#undef DG_QUARTER
 #undef DG_ROWS
 #undef DG_LOAD_BF
 #undef DG_FRAG
+#undef DG_PREFETCH
 #undef DG_ISSUE_B
 #undef DG_ISSUE_A
 
-    // ---- epilogue.  Lane holds row (16i + lr), columns (16j + 4lg .. +3) of
-    // its wave tile.  Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage
+    // ---- epilogue.  Lane holds tile row 16 (WAVES_M i + wm) + lr and
+    // columns wcol + 16j + 4lg .. +3.  Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage
     // the whole tile in LDS, then write it back in full 16-byte chunks.  In
     // LDS, 16-byte chunk c of row r sits at c ^ (r & 15): the 16 rows a
     // fragment store touches land in distinct banks.
@@ -365,7 +421,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     uint8_t* const sD = smem;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
-        const int row = wrow + 16 * i + lr;
+        const int row = 16 * (T::WAVES_M * i + wm) + lr;
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int col = wcol + 16 * j + 4 * lg;
@@ -411,15 +467,17 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 }
 
 // 256x256 tiles, 8 waves of 128x64 (two per SIMD).
-using TileLarge = TileConfig<256, 256, 2, 4, 4>;
-// 128x256 tiles, 4 waves of 128x64: contiguous groups are padded to 128 rows.
-using TileRows128 = TileConfig<128, 256, 1, 4, 8>;
+using TileLarge = TileConfig<256, 256, 2, 4, 4, false, DG_PF_DENSE>;
+// 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows.
+using TileRows128 = TileConfig<128, 256, 2, 4, 8, false, DG_PF_CONTIG>;
+// 256x256 tiles with row skipping: masked groups end anywhere.
+using TileMasked = TileConfig<256, 256, 2, 4, 4, true, DG_PF_MASKED>;
 
 hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
     switch (form) {
         case Form::Dense: return launch_tiled<TileLarge, Form::Dense>(a, stream);
         case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous>(a, stream);
-        case Form::Masked: return launch_tiled<TileLarge, Form::Masked>(a, stream);
+        case Form::Masked: return launch_tiled<TileMasked, Form::Masked>(a, stream);
     }
     return hipErrorInvalidValue;
 }
