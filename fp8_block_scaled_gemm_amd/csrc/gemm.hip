@@ -33,6 +33,8 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 namespace dg {
 
@@ -67,19 +69,27 @@ struct TileConfig {
     // that come from HBM need more bytes in flight than two LDS stages hold.
     static constexpr int kPrefetch = PREFETCH_;
     static constexpr int kPrefetchOps = PREFETCH_ > 0 ? 2 : 0;
-    // one wave-wide direct load fills 1 KiB (8 rows) of a stage
+    // one wave-wide direct load fills 1 KiB (8 rows) of a stage; waves take
+    // the 8-row groups round-robin (the B slab may end part way round)
     static constexpr int kLoadsA = BM / 8 / kWaves;
-    static constexpr int kLoadsB = BN / 8 / kWaves;
+    static constexpr int kLoadsB = (BN / 8 + kWaves - 1) / kWaves;
     static constexpr int kStageA = BM * 128;
     static constexpr int kStageB = BN * 128;
+    // every wave's columns lie in one 128-column scale block
+    static constexpr bool kOneScaleB = BN % 128 == 0 && 128 % WN == 0;
+    // LDS row pitch of the bf16 output tile: a power of two of 16-byte
+    // chunks, at least 16, so the chunk swizzle c ^ (row & 15) stays in the row
+    static constexpr int kPitchChunks = BN <= 128 ? 16 : 32;
     // the bf16 output tile reuses the stage memory on its way out
-    static constexpr int kSmem = (2 * (kStageA + kStageB) > BM * BN * 2) ? 2 * (kStageA + kStageB)
-                                                                         : BM * BN * 2;
+    static constexpr int kSmem = (2 * (kStageA + kStageB) > BM * kPitchChunks * 16)
+                                     ? 2 * (kStageA + kStageB)
+                                     : BM * kPitchChunks * 16;
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16x16");
-    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "uneven slab staging");
-    static_assert(BN % 128 == 0 && 128 % WN == 0, "a wave's columns share one column-scale block");
+    static_assert(BM % (8 * kWaves) == 0 && BN % 8 == 0, "slabs are staged 8 rows at a time");
+    static_assert(BN <= 256, "output tile pitch");
     static_assert(BM % 64 == 0 && kWaves % (BM / 64) == 0, "waves stage the A scales 64 rows each");
-    static_assert(BM <= 32 * kWaves && BN <= 32 * kWaves, "a wave's prefetch covers 32 rows of a slab");
+    static_assert(PREFETCH_ == 0 || (BM <= 32 * kWaves && BN <= 32 * kWaves),
+                  "a wave's prefetch covers 32 rows of a slab");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -168,6 +178,59 @@ struct TileInfo {
     uint64_t ok0, ok1;  // contiguous form: routed-row masks, tile rows 0-63 / 64-127
 };
 
+// Masked form: work units are (group, m-block) pairs times n-blocks; a
+// pair's cost is the number of 64-row chunks of its m-block that hold valid
+// rows.  Pairs are ranked by cost, highest first (ties by pair index); rank r
+// goes to XCD r % 8, so every XCD gets a balanced share, runs its pairs
+// longest first, and keeps all n-blocks of a pair (which share the A rows) in
+// its own L2.  Workgroup b runs on XCD b % 8 as that XCD's (b / 8)-th tile.
+// Pairs without valid rows rank last and are skipped.  Every lane of the
+// wave computes the same answer from the masked_m array.
+template <class T>
+__device__ __forceinline__ bool masked_slot(int b, int m_blocks, int n_blocks, int64_t rows,
+                                            int G, const int32_t* __restrict__ masked_m,
+                                            int lane, int& g, int& mb, int& nb) {
+    constexpr int kLevels = T::BM / 64 + 1;  // costs 0 .. BM/64
+    const int P = G * m_blocks;
+    const int k = b / kNumXcds;
+    const int slot = (k / n_blocks) * kNumXcds + b % kNumXcds;  // the pair's rank
+    if (slot >= P) return false;
+    nb = k % n_blocks;
+    auto cost = [&](int q) {
+        const int64_t vm = min<int64_t>(max(masked_m[q / m_blocks], 0), rows);
+        const int64_t v = min<int64_t>(max<int64_t>(vm - (int64_t)(q % m_blocks) * T::BM, 0), T::BM);
+        return (int)((v + 63) >> 6);
+    };
+    int count[kLevels];
+#pragma unroll
+    for (int L = 0; L < kLevels; ++L) count[L] = 0;
+    for (int base = 0; base < P; base += 64) {
+        const int q = base + lane;
+        const int c = q < P ? cost(q) : -1;
+#pragma unroll
+        for (int L = 0; L < kLevels; ++L) count[L] += __popcll(__ballot(c == L));
+    }
+    int level = kLevels - 1, pos = slot;
+    while (level > 0 && pos >= count[level]) pos -= count[level--];
+    if (level == 0) return false;
+    for (int base = 0; base < P; base += 64) {
+        const int q = base + lane;
+        const bool hit = q < P && cost(q) == level;
+        const uint64_t m = __ballot(hit);
+        const int n = __popcll(m);
+        if (pos < n) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const int q_sel = base + __builtin_ctzll(__ballot(hit && below == pos));
+            g = q_sel / m_blocks;
+            mb = q_sel % m_blocks;
+            return true;
+        }
+        pos -= n;
+    }
+    return false;
+}
+
 // Decode workgroup `b`'s tile; false when it is a padding slot or the tile
 // has no routed row (masked rows past masked_m, contiguous blocks of
 // padding).  Contiguous: the block's group is the largest id in [0, G) among
@@ -177,15 +240,21 @@ template <class T, Form kForm>
 __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, int64_t rows,
                                             int64_t G, const int32_t* __restrict__ aux,
                                             int lane, TileInfo& ti) {
-    const int tiles_per_group = m_blocks * n_blocks;
-    const int groups = kForm == Form::Masked ? (int)G : 1;
-    int tile = xcd_tile(b, groups * tiles_per_group);
+    ti.ok0 = ti.ok1 = 0;
+    if (kForm == Form::Masked) {
+        int mb, nb;
+        if (!masked_slot<T>(b, m_blocks, n_blocks, rows, (int)G, aux, lane, ti.g, mb, nb))
+            return false;
+        ti.m0 = mb * T::BM;
+        ti.n0 = nb * T::BN;
+        const int64_t vm = min<int64_t>(max(aux[ti.g], 0), rows);
+        ti.valid = (int)min<int64_t>(T::BM, vm - ti.m0);
+        ti.arow0 = (int64_t)ti.g * rows + ti.m0;
+        return true;
+    }
+    int tile = xcd_tile(b, m_blocks * n_blocks);
     if (tile < 0) return false;
     ti.g = 0;
-    if (kForm == Form::Masked) {
-        ti.g = tile / tiles_per_group;
-        tile -= ti.g * tiles_per_group;
-    }
     // raster: groups of kGroupM m-blocks, m fastest inside a group
     const int span = T::kGroupM * n_blocks;
     const int first_m = (tile / span) * T::kGroupM;
@@ -193,15 +262,9 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
     const int in_span = tile % span;
     ti.m0 = (first_m + in_span % gm) * T::BM;
     ti.n0 = (in_span / gm) * T::BN;
-    ti.ok0 = ti.ok1 = 0;
     if (kForm == Form::Dense) {
         ti.valid = (int)min<int64_t>(T::BM, rows - ti.m0);
         ti.arow0 = ti.m0;
-    } else if (kForm == Form::Masked) {
-        const int64_t vm = min<int64_t>(max(aux[ti.g], 0), rows);
-        if (ti.m0 >= vm) return false;
-        ti.valid = (int)min<int64_t>(T::BM, vm - ti.m0);
-        ti.arow0 = (int64_t)ti.g * rows + ti.m0;
     } else {
         static_assert(kForm != Form::Contiguous || T::BM == 128, "one group per 128-row block");
         const int id0 = aux[ti.m0 + lane], id1 = aux[ti.m0 + 64 + lane];
@@ -238,10 +301,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
     const float* __restrict__ sb, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
     int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks, int n_blocks) {
-    // Two A stages then two B stages (after the K loop: the bf16 output tile);
-    // two stages of A row scales and of column-block scales.
+    // Two A stages then two B stages (after the K loop: the bf16 output tile).
+    // Scales come in chunks of four K blocks, two chunk buffers: row scales
+    // as [row][4], column-block scales as [block][4].
     __shared__ __align__(1024) uint8_t smem[T::kSmem];
-    __shared__ __align__(16) float smSA[2][T::BM];
+    __shared__ __align__(16) float smSA[2][T::BM * 4];
     __shared__ __align__(16) float smSB[2][64];
     __shared__ __align__(16) float smPF[64];  // sink of the prefetch loads, never read
 
@@ -268,12 +332,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // count towards the wave's vmcnt like every other step's.
     const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
     const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
-    const int sa_rows = (wave % (T::BM / 64)) * 64;
-    const uint32_t offSA = (uint32_t)(sa_rows + lane) * (uint32_t)KB * 4;
-    const uint32_t offSB = (uint32_t)lane * (uint32_t)KB * 4;
+    // scale chunk loads: wave w < BM/64 fetches 16 bytes (four K blocks) of
+    // the row scales of rows [64w, 64w + 64), the next wave the column-block
+    // scales (lane l: block l / 4, K block l % 4 of the chunk)
+    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)KB * 4;
+    const uint32_t offSB = ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
+    constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
+    static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
     const int nb0 = ti.n0 >> 7;
     const int vn = (int)min<int64_t>(T::BN, N - ti.n0);
-    const int vnb = min(T::BN / 128, NB - nb0);  // column-scale blocks the tile touches
+    // column-scale blocks the tile touches
+    const int vnb = (int)((ti.n0 + vn - 1) >> 7) - nb0 + 1;
     const uint8_t* tileA = A + ti.arow0 * K;
     const float* tileSA = sa + ti.arow0 * KB;
     const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
@@ -287,19 +356,34 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
                                     live_ ? (uint32_t)max(ti.valid - r0, 0) * (uint32_t)K : 0u),  \
                         offRow, smA + (st_) * T::kStageA + (wave + i * T::kWaves) * 1024);        \
         }                                                                                         \
-        load_lds_4(buffer_rsrc(tileSA + (kb_), live_ ? (uint32_t)ti.valid * KB * 4 : 0u), offSA,  \
-                   &smSA[st_][sa_rows]);                                                          \
-        load_lds_4(buffer_rsrc(tileSB + (kb_), live_ ? (uint32_t)vnb * KB * 4 - (kb_) * 4 : 0u),   \
-                   offSB, &smSB[st_][0]);                                                         \
     } while (0)
 #define DG_ISSUE_B(kb_, st_)                                                                      \
     do {                                                                                          \
         const bool live_ = (kb_) < KB;                                                            \
         _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
             const int r0 = i * T::kWaves * 8;                                                     \
+            if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;         \
             load_lds_16(buffer_rsrc(tileB + (int64_t)r0 * K + (kb_) * 128,                        \
                                     live_ ? (uint32_t)max(vn - r0, 0) * (uint32_t)K : 0u),        \
                         offRow, smB + (st_) * T::kStageB + (wave + i * T::kWaves) * 1024);        \
+        }                                                                                         \
+    } while (0)
+
+    // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1.  The
+    // range check of a buffer load is per 4-byte word, so the words of a row's
+    // last chunk past K/128 (and rows past the valid ones) read as zero or as
+    // the next row's scales, which no step uses.
+#define DG_ISSUE_SCALES(c_)                                                                       \
+    do {                                                                                          \
+        const int kb0_ = (c_) * 4;                                                                \
+        if (kb0_ < KB) {                                                                          \
+            if (wave < kScaleWaves) {                                                             \
+                load_lds_16(buffer_rsrc(tileSA + kb0_, (uint32_t)(ti.valid * KB - kb0_) * 4),    \
+                            offSA, &smSA[(c_) & 1][wave * 64 * 4]);                               \
+            } else if (wave == kScaleWaves) {                                                     \
+                load_lds_4(buffer_rsrc(tileSB + kb0_, (uint32_t)(vnb * KB - kb0_) * 4),          \
+                           lane < 4 * vnb ? offSB : 0xffffff00u, &smSB[(c_) & 1][0]);             \
+            }                                                                                     \
         }                                                                                         \
     } while (0)
 
@@ -331,7 +415,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const int srow = 16 * wm + lr;
     // sub-tile rows of this wave that hold valid rows; the others are skipped
     const int vsub = (ti.valid - 16 * wm + kRowStep - 1) / kRowStep;
-    const int sblk = wcol >> 7;  // the wave's column-scale block within the tile
+    // column-scale block of sub-tile j, relative to the tile's first one
+    int sblk[T::TN];
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) sblk[j] = (int)((ti.n0 + wcol + 16 * j) >> 7) - nb0;
 #define DG_FRAG(base_, off_)                                                                      \
     join(*reinterpret_cast<const v4u*>((base_) + (off_) + chunk_lo),                             \
          *reinterpret_cast<const v4u*>((base_) + (off_) + chunk_hi))
@@ -348,22 +435,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_
-#define DG_ROWS(bf_use, st_, i0_, i1_)                                                            \
+#define DG_ROWS(bf_use, kb_, st_, i0_, i1_)                                                       \
     do {                                                                                          \
-        const float s_b_ = smSB[st_][sblk];                                                       \
+        const float* sSA_ = &smSA[((kb_) >> 2) & 1][(kb_) & 3];                                   \
+        const float* sSB_ = &smSB[((kb_) >> 2) & 1][(kb_) & 3];                                   \
+        float s_b_[T::kOneScaleB ? 1 : T::TN];                                                    \
+        _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)                   \
+            s_b_[j] = sSB_[sblk[j] * 4];                                                          \
         _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
             const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);       \
-            const float s_ = smSA[st_][srow + kRowStep * i] * s_b_;                               \
+            const float s_a_ = sSA_[(srow + kRowStep * i) * 4];                                   \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
-                acc[i][j] += s_ * mfma_block(bf_use[j], af_);                                     \
+                acc[i][j] += (s_a_ * s_b_[T::kOneScaleB ? 0 : j]) * mfma_block(bf_use[j], af_);   \
         }                                                                                         \
     } while (0)
     // With kRowSkip, a quarter of the sub-tile rows runs only when it holds
     // valid rows: one uniform branch per quarter.
-#define DG_QUARTER(bf_use, st_, q_)                                                               \
+#define DG_QUARTER(bf_use, kb_, st_, q_)                                                          \
     do {                                                                                          \
         if (!T::kRowSkip || (q_) == 0 || vsub > (q_) * (T::TM / 4))                               \
-            DG_ROWS(bf_use, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4));                  \
+            DG_ROWS(bf_use, kb_, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4));             \
     } while (0)
 
     // One K block kb_ on stages st_ (= kb_ & 1).  The B fragments of block
@@ -376,16 +467,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         DG_ISSUE_A((kb_) + 1, (st_) ^ 1);                                                         \
         DG_ISSUE_B((kb_) + 2, (st_));                                                             \
         DG_PREFETCH((kb_) + 1 + T::kPrefetch, (kb_) + 2 + T::kPrefetch);                          \
-        DG_QUARTER(bf_use, st_, 0);                                                               \
-        DG_QUARTER(bf_use, st_, 1);                                                               \
+        if (((kb_) & 3) == 0) DG_ISSUE_SCALES(((kb_) >> 2) + 1);                                  \
+        DG_QUARTER(bf_use, kb_, st_, 0);                                                          \
+        DG_QUARTER(bf_use, kb_, st_, 1);                                                          \
         DG_LOAD_BF(bf_next, (st_) ^ 1);                                                           \
-        DG_QUARTER(bf_use, st_, 2);                                                               \
-        DG_QUARTER(bf_use, st_, 3);                                                               \
+        DG_QUARTER(bf_use, kb_, st_, 2);                                                          \
+        DG_QUARTER(bf_use, kb_, st_, 3);                                                          \
         wait_vmcnt_lgkm0<T::kPrefetchOps>();                                                      \
         lds_barrier();                                                                            \
     } while (0)
 
     v8i bf0[T::TN], bf1[T::TN];
+    DG_ISSUE_SCALES(0);
     DG_ISSUE_A(0, 0);
     DG_ISSUE_B(0, 0);
     DG_ISSUE_B(1, 1);
@@ -405,17 +498,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 #undef DG_LOAD_BF
 #undef DG_FRAG
 #undef DG_PREFETCH
+#undef DG_ISSUE_SCALES
 #undef DG_ISSUE_B
 #undef DG_ISSUE_A
 
     // ---- epilogue.  Lane holds tile row 16 (WAVES_M i + wm) + lr and
-    // columns wcol + 16j + 4lg .. +3.  Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage
-    // the whole tile in LDS, then write it back in full 16-byte chunks.  In
-    // LDS, 16-byte chunk c of row r sits at c ^ (r & 15): the 16 rows a
-    // fragment store touches land in distinct banks.
-    constexpr int kRowBytes = T::BN * 2;
-    constexpr int kChunks = kRowBytes / 16;
-    static_assert(kChunks % 16 == 0 && 64 % kChunks == 0, "row chunking");
+    // columns wcol + 16j + 4lg .. +3.  Round to bf16 (v_cvt_pk_bf16_f32:
+    // nearest even), stage the whole tile in LDS, then write it back in full
+    // 16-byte chunks, consecutive lanes on consecutive chunks of a row.  In
+    // LDS (row pitch kPitchChunks chunks), 16-byte chunk c of row r sits at
+    // c ^ (r & 15): the 16 rows a fragment store touches land in distinct banks.
+    constexpr int kRowBytes = T::kPitchChunks * 16;
+    constexpr int kChunks = T::BN / 8;  // 16-byte chunks of an output row
     wait_vmcnt<0>();  // the empty loads of the last steps have retired
     lds_barrier();
     uint8_t* const sD = smem;
@@ -435,16 +529,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         }
     }
     __syncthreads();
-    constexpr int kRowsPerPass = 64 / kChunks;  // rows one wave-wide access covers
-    const int prow = lane / kChunks, pchunk = lane % kChunks;
-    const int64_t col = ti.n0 + pchunk * 8;
+    static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
 #pragma unroll 4
-    for (int r = wave * kRowsPerPass; r < T::BM; r += T::kWaves * kRowsPerPass) {
-        const int row = r + prow;
+    for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
+        const int row = q / kChunks, c = q % kChunks;
+        const int64_t col = ti.n0 + c * 8;
         bool ok = row < ti.valid && col < N;
         if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
-        const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes +
-                                                    ((pchunk ^ (row & 15)) << 4));
+        const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
         if (ok) *reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col) = v;
     }
 }
@@ -453,10 +545,14 @@ template <class T, Form kForm>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t m_blocks = (a.rows + T::BM - 1) / T::BM;
     const int64_t n_blocks = (a.N + T::BN - 1) / T::BN;
-    const int64_t groups = (kForm == Form::Masked) ? a.G : 1;
-    const int64_t tiles = groups * m_blocks * n_blocks;
-    if (tiles == 0) return hipSuccess;
-    const int64_t grid = (tiles + kNumXcds - 1) / kNumXcds * kNumXcds;
+    int64_t grid;
+    if (kForm == Form::Masked) {
+        // every XCD gets ceil(pairs / 8) pairs of n_blocks tiles
+        grid = (a.G * m_blocks + kNumXcds - 1) / kNumXcds * n_blocks * kNumXcds;
+    } else {
+        grid = (m_blocks * n_blocks + kNumXcds - 1) / kNumXcds * kNumXcds;
+    }
+    if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     // per-lane 32-bit offsets: a tile's rows of K bytes, its A scales
     if ((int64_t)std::max(T::BM, T::BN) * a.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
@@ -468,14 +564,75 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 
 // 256x256 tiles, 8 waves of 128x64 (two per SIMD).
 using TileLarge = TileConfig<256, 256, 2, 4, 4, false, DG_PF_DENSE>;
-// 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows.
+// Narrower dense tiles, 8 waves of 64x112 / 64x96: fewer idle CUs in the
+// last round of tiles when N is not a good multiple of 256.
+using TileWide224 = TileConfig<256, 224, 4, 2, 4, false, 0>;
+using TileWide192 = TileConfig<256, 192, 4, 2, 4, false, 0>;
+// 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
+// also the dense shape for few rows.
 using TileRows128 = TileConfig<128, 256, 2, 4, 8, false, DG_PF_CONTIG>;
-// 256x256 tiles with row skipping: masked groups end anywhere.
-using TileMasked = TileConfig<256, 256, 2, 4, 4, true, DG_PF_MASKED>;
+// Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
+// MFMAs of invalid rows does not shorten them.
+using TileMasked = TileConfig<256, 256, 2, 4, 4, false, DG_PF_MASKED>;
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64) cached[dev] = n;
+    return n;
+}
+
+// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256 pins the dense tile
+// shape (for tests and tuning; read at every call); -1 when unset or not
+// one of these.
+static int forced_dense_shape() {
+    const char* e = getenv("DG_FP8_DENSE_TILE");
+    if (!e) return -1;
+    const char* names[] = {"256x256", "256x224", "256x192", "128x256"};
+    for (int i = 0; i < 4; ++i)
+        if (strcmp(e, names[i]) == 0) return i;
+    return -1;
+}
+
+// Dense tile shape: one workgroup per CU at a time, so a launch takes about
+// ceil(tiles / CUs) rounds of one tile's time.  A tile's time scales with its
+// area times a per-shape cost per output element (narrower tiles re-read
+// more fragments per MFMA); pick the shape with the least estimated time.
+hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
+    struct Shape { int bm, bn; double rel; };
+    static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.05}, {256, 192, 1.10},
+                                    {128, 256, 1.15}};
+    const int64_t cus = device_cus();
+    int best = forced_dense_shape();
+    if (best < 0) {
+        double best_cost = 0;
+        for (int i = 0; i < 4; ++i) {
+            const Shape& sh = kShapes[i];
+            const int64_t tiles = ((a.rows + sh.bm - 1) / sh.bm) * ((a.N + sh.bn - 1) / sh.bn);
+            const double cost = (double)((tiles + cus - 1) / cus) * sh.bm * sh.bn * sh.rel;
+            if (i == 0 || cost < best_cost) {
+                best_cost = cost;
+                best = i;
+            }
+        }
+    }
+    switch (best) {
+        case 1: return launch_tiled<TileWide224, Form::Dense>(a, stream);
+        case 2: return launch_tiled<TileWide192, Form::Dense>(a, stream);
+        case 3: return launch_tiled<TileRows128, Form::Dense>(a, stream);
+        default: return launch_tiled<TileLarge, Form::Dense>(a, stream);
+    }
+}
 
 hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
     switch (form) {
-        case Form::Dense: return launch_tiled<TileLarge, Form::Dense>(a, stream);
+        case Form::Dense: return launch_dense(a, stream);
         case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous>(a, stream);
         case Form::Masked: return launch_tiled<TileMasked, Form::Masked>(a, stream);
     }

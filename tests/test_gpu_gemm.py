@@ -96,6 +96,15 @@ def test_dense_parity(orc, M, N, K):
     _check_full(orc, dense_case(M, N, K, seed=M * 7 + N + K, name=f"dense_{M}x{N}x{K}"))
 
 
+@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256"])
+@pytest.mark.parametrize("M,N,K", [(300, 488, 384), (512, 448, 256), (40, 200, 128)])
+def test_dense_tile_shapes(orc, monkeypatch, tile, M, N, K):
+    # every dense tile shape on ragged and exact sizes: several tiles, a
+    # partial last tile in M and N, tiles straddling column-scale blocks
+    monkeypatch.setenv("DG_FP8_DENSE_TILE", tile)
+    _check_full(orc, dense_case(M, N, K, seed=M + N + K))
+
+
 def test_dense_parity_scaled_rows(orc):
     """Rows with very different magnitudes: per-row scales span 2^-20..2^20."""
     case = dense_case(200, 264, 512, seed=5)
@@ -136,6 +145,20 @@ def test_masked_parity(orc, masked):
 
 def test_masked_out_of_range_counts_are_clamped(orc):
     _check_full(orc, masked_case(3, 64, 24, 256, seed=2, masked=[-5, 1000, 64]))
+
+
+def test_masked_many_groups(orc):
+    # more (group, m-block) pairs than lanes in a wave, with ties and empty groups
+    rng = np.random.default_rng(70)
+    masked = [int(x) for x in rng.integers(0, 41, size=70)]
+    masked[3] = masked[9] = 40
+    masked[5] = 0
+    _check_full(orc, masked_case(70, 40, 136, 256, seed=70, masked=masked))
+
+
+def test_masked_several_m_blocks(orc):
+    # groups taller than one tile: a group's m-blocks carry different costs
+    _check_full(orc, masked_case(3, 600, 136, 256, seed=600, masked=[600, 257, 513]))
 
 
 def test_masked_all_zero_leaves_d_untouched(orc):
