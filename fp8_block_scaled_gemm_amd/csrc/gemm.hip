@@ -40,18 +40,8 @@ namespace dg {
 
 constexpr int kNumXcds = 8;
 
-#ifndef DG_PF_DENSE
-#define DG_PF_DENSE 0
-#endif
-#ifndef DG_PF_CONTIG
-#define DG_PF_CONTIG 0
-#endif
-#ifndef DG_PF_MASKED
-#define DG_PF_MASKED 0
-#endif
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_, bool ROW_SKIP_,
-          int PREFETCH_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_, bool ROW_SKIP_>
 struct TileConfig {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -63,16 +53,11 @@ struct TileConfig {
     // skip the MFMAs of sub-tile rows past the tile's valid rows, a quarter
     // of the wave tile at a time (worth it where tiles are often partial)
     static constexpr bool kRowSkip = ROW_SKIP_;
-    // Besides the slabs of the next blocks (landing in LDS), each step asks
-    // for the cache lines of the slabs kPrefetch blocks further ahead, so
-    // that they are on chip when their slab load is issued (0: off).  Streams
-    // that come from HBM need more bytes in flight than two LDS stages hold.
-    static constexpr int kPrefetch = PREFETCH_;
-    static constexpr int kPrefetchOps = PREFETCH_ > 0 ? 2 : 0;
     // one wave-wide direct load fills 1 KiB (8 rows) of a stage; waves take
     // the 8-row groups round-robin (the B slab may end part way round)
     static constexpr int kLoadsA = BM / 8 / kWaves;
     static constexpr int kLoadsB = (BN / 8 + kWaves - 1) / kWaves;
+    static constexpr int kLoadsBMin = BN / 8 / kWaves;  // loads of the wave with the fewest
     static constexpr int kStageA = BM * 128;
     static constexpr int kStageB = BN * 128;
     // every wave's columns lie in one 128-column scale block
@@ -88,8 +73,6 @@ struct TileConfig {
     static_assert(BM % (8 * kWaves) == 0 && BN % 8 == 0, "slabs are staged 8 rows at a time");
     static_assert(BN <= 256, "output tile pitch");
     static_assert(BM % 64 == 0 && kWaves % (BM / 64) == 0, "waves stage the A scales 64 rows each");
-    static_assert(PREFETCH_ == 0 || (BM <= 32 * kWaves && BN <= 32 * kWaves),
-                  "a wave's prefetch covers 32 rows of a slab");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -115,15 +98,18 @@ __device__ __forceinline__ v4u buffer_rsrc(const void* base, uint32_t bytes) {
 // assembly on purpose: the compiler then does not track these LDS writes and
 // cannot put a wait for the stage being filled in front of reads of the
 // other stage (its alias tracking for such loads depends on control flow).
-// The kernel orders them itself with explicit vmcnt waits before the barrier
-// that publishes a stage.
+// The kernel orders them itself: every LDS read of a buffer is separated
+// from the loads that refill it by a barrier (a compiler memory barrier as
+// well), and a buffer is read only after the explicit vmcnt wait and barrier
+// that publish it.  So the statements carry no memory clobber, and the
+// compiler may still schedule unrelated LDS reads and arithmetic across them.
 __device__ __forceinline__ void load_lds_16(const v4u& rsrc, uint32_t off, void* dst) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "memory", "m0");
+                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "m0");
 }
 __device__ __forceinline__ void load_lds_4(const v4u& rsrc, uint32_t off, void* dst) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "memory", "m0");
+                 :: "s"(lds_addr(dst)), "v"(off), "s"(rsrc) : "m0");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt bits
@@ -307,7 +293,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     __shared__ __align__(1024) uint8_t smem[T::kSmem];
     __shared__ __align__(16) float smSA[2][T::BM * 4];
     __shared__ __align__(16) float smSB[2][64];
-    __shared__ __align__(16) float smPF[64];  // sink of the prefetch loads, never read
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,9 +311,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 
     // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
     // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
-    // belongs at physical chunk l % 8.  Each load's buffer starts at its first
-    // row and ends at the tile's last valid row (A) or column (B); blocks past
-    // the last one get an empty buffer, so their loads move no data but still
+    // belongs at physical chunk l % 8.  A slab's buffer starts at the K block
+    // in row 0 and ends with the tile's last valid row (A) or column (B), so
+    // rows past it read as zero; blocks past the last one get an empty
+    // buffer, so their loads move no data but still
     // count towards the wave's vmcnt like every other step's.
     const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
     const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
@@ -347,25 +333,25 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const float* tileSA = sa + ti.arow0 * KB;
     const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
     const float* tileSB = sb + ((int64_t)ti.g * NB + nb0) * KB;
-#define DG_ISSUE_A(kb_, st_)                                                                      \
+#define DG_ISSUE_A_PART(kb_, st_, i0_, i1_)                                                       \
     do {                                                                                          \
-        const bool live_ = (kb_) < KB;                                                            \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsA; ++i) {                                  \
-            const int r0 = i * T::kWaves * 8;                                                     \
-            load_lds_16(buffer_rsrc(tileA + (int64_t)r0 * K + (kb_) * 128,                        \
-                                    live_ ? (uint32_t)max(ti.valid - r0, 0) * (uint32_t)K : 0u),  \
-                        offRow, smA + (st_) * T::kStageA + (wave + i * T::kWaves) * 1024);        \
-        }                                                                                         \
+        const v4u rs_ = buffer_rsrc(tileA + (kb_) * 128,                                          \
+                                    (kb_) < KB ? (uint32_t)ti.valid * (uint32_t)K - (kb_) * 128 : 0u); \
+        _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i)                                     \
+            load_lds_16(rs_, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,                \
+                        smA + (st_) * T::kStageA + (wave + i * T::kWaves) * 1024);                \
     } while (0)
+    // rows [0, BM/2) and [BM/2, BM) of the A slab
+#define DG_ISSUE_AL(kb_, st_) DG_ISSUE_A_PART(kb_, st_, 0, T::kLoadsA / 2)
+#define DG_ISSUE_AH(kb_, st_) DG_ISSUE_A_PART(kb_, st_, T::kLoadsA / 2, T::kLoadsA)
 #define DG_ISSUE_B(kb_, st_)                                                                      \
     do {                                                                                          \
-        const bool live_ = (kb_) < KB;                                                            \
+        const v4u rs_ = buffer_rsrc(tileB + (kb_) * 128,                                          \
+                                    (kb_) < KB ? (uint32_t)vn * (uint32_t)K - (kb_) * 128 : 0u);  \
         _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
-            const int r0 = i * T::kWaves * 8;                                                     \
             if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;         \
-            load_lds_16(buffer_rsrc(tileB + (int64_t)r0 * K + (kb_) * 128,                        \
-                                    live_ ? (uint32_t)max(vn - r0, 0) * (uint32_t)K : 0u),        \
-                        offRow, smB + (st_) * T::kStageB + (wave + i * T::kWaves) * 1024);        \
+            load_lds_16(rs_, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,                \
+                        smB + (st_) * T::kStageB + (wave + i * T::kWaves) * 1024);                \
         }                                                                                         \
     } while (0)
 
@@ -384,22 +370,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
                 load_lds_4(buffer_rsrc(tileSB + kb0_, (uint32_t)(vnb * KB - kb0_) * 4),          \
                            lane < 4 * vnb ? offSB : 0xffffff00u, &smSB[(c_) & 1][0]);             \
             }                                                                                     \
-        }                                                                                         \
-    } while (0)
-
-    // Prefetch: wave w asks for one 4-byte word in each of the 128-byte lines
-    // of rows [32w, 32w + 32) of the A slab and of the B slab (lanes 32-63
-    // point past every buffer and move nothing).
-    const uint32_t offPF = lane < 32 ? (uint32_t)(32 * wave + lane) * (uint32_t)K : 0xffffff00u;
-#define DG_PREFETCH(kba_, kbb_)                                                                   \
-    do {                                                                                          \
-        if (T::kPrefetch > 0) {                                                                   \
-            load_lds_4(buffer_rsrc(tileA + (kba_) * 128,                                          \
-                                   (kba_) < KB ? (uint32_t)ti.valid * (uint32_t)K : 0u),          \
-                       offPF, smPF);                                                              \
-            load_lds_4(buffer_rsrc(tileB + (kbb_) * 128,                                          \
-                                   (kbb_) < KB ? (uint32_t)vn * (uint32_t)K : 0u),                \
-                       offPF, smPF);                                                              \
         }                                                                                         \
     } while (0)
 
@@ -457,50 +427,69 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
             DG_ROWS(bf_use, kb_, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4));             \
     } while (0)
 
-    // One K block kb_ on stages st_ (= kb_ & 1).  The B fragments of block
-    // kb_+1 are read in the middle of the step, between the two halves of
-    // the rows; the step ends by waiting for this wave's slab loads (A of
-    // kb_+1, B of kb_+2) and for its LDS reads, then the barrier publishes
-    // the new slabs and frees the ones this step read.
-#define DG_STEP(bf_use, bf_next, kb_, st_)                                                        \
+    // One K block kb_ on stages st_ (= kb_ & 1), in two halves separated by
+    // a barrier.  The step starts by reading its B fragments (B slab of kb_);
+    // the first half multiplies the A rows [0, BM/2), the second half the rows
+    // [BM/2, BM).  A slab load is issued as soon as the barrier that frees its
+    // buffer has passed:
+    //   after the mid barrier: A rows [0, BM/2) and the B slab of block kb_+2
+    //     (their buffers held those of kb_);
+    //   after the end barrier: A rows [BM/2, BM) of block kb_+2.
+    // So every load has one and a half steps to land.  Loads of a wave
+    // complete in issue order; a barrier publishes what it needs by waiting
+    // until at most the loads issued after those (kAfter) remain.  Scale
+    // chunk loads (some waves, every fourth step) only make a wait stricter.
+#define DG_STEP(kb_, st_)                                                                         \
     do {                                                                                          \
-        DG_ISSUE_A((kb_) + 1, (st_) ^ 1);                                                         \
-        DG_ISSUE_B((kb_) + 2, (st_));                                                             \
-        DG_PREFETCH((kb_) + 1 + T::kPrefetch, (kb_) + 2 + T::kPrefetch);                          \
-        if (((kb_) & 3) == 0) DG_ISSUE_SCALES(((kb_) >> 2) + 1);                                  \
-        DG_QUARTER(bf_use, kb_, st_, 0);                                                          \
-        DG_QUARTER(bf_use, kb_, st_, 1);                                                          \
-        DG_LOAD_BF(bf_next, (st_) ^ 1);                                                           \
-        DG_QUARTER(bf_use, kb_, st_, 2);                                                          \
-        DG_QUARTER(bf_use, kb_, st_, 3);                                                          \
-        wait_vmcnt_lgkm0<T::kPrefetchOps>();                                                      \
+        DG_LOAD_BF(bf, (st_));                                                                    \
+        DG_QUARTER(bf, kb_, st_, 0);                                                              \
+        DG_QUARTER(bf, kb_, st_, 1);                                                              \
+        wait_vmcnt_lgkm0<kAfter>(); /* A rows [BM/2, BM) of kb_ */                                \
         lds_barrier();                                                                            \
+        DG_ISSUE_AL((kb_) + 2, (st_));                                                            \
+        DG_ISSUE_B((kb_) + 2, (st_));                                                             \
+        if (((kb_) & 3) == 0) DG_ISSUE_SCALES(((kb_) >> 2) + 1);                                  \
+        DG_QUARTER(bf, kb_, st_, 2);                                                              \
+        DG_QUARTER(bf, kb_, st_, 3);                                                              \
+        wait_vmcnt_lgkm0<kAfter>(); /* A rows [0, BM/2) and B of kb_+1 */                         \
+        lds_barrier();                                                                            \
+        DG_ISSUE_AH((kb_) + 2, (st_));                                                            \
     } while (0)
 
-    v8i bf0[T::TN], bf1[T::TN];
+    // Loads a wave issues after the ones a barrier waits for (see above),
+    // counted for the wave that issues the fewest B loads.
+    constexpr int kAfter = T::kLoadsA + T::kLoadsBMin;
+    static_assert(T::kLoadsA % 2 == 0 && kAfter < 64, "A slab halves, vmcnt range");
+
+    v8i bf[T::TN];
+    // Prologue: blocks 0 and 1 of A rows [0, BM/2) and of B, A rows
+    // [BM/2, BM) of block 0 and scale chunk 0 land and are published; A rows
+    // [BM/2, BM) of block 1 go last, as in the steady state, so that the
+    // first waits count the same loads.
     DG_ISSUE_SCALES(0);
-    DG_ISSUE_A(0, 0);
+    DG_ISSUE_AL(0, 0);
+    DG_ISSUE_AH(0, 0);
     DG_ISSUE_B(0, 0);
+    DG_ISSUE_AL(1, 1);
     DG_ISSUE_B(1, 1);
     wait_vmcnt<0>();
     lds_barrier();
-    DG_LOAD_BF(bf0, 0);
-    wait_vmcnt_lgkm0<0>();  // B stage 0 is read before step 0 refills it
-    lds_barrier();
+    DG_ISSUE_AH(1, 1);
 
     for (int kb = 0; kb < KB; kb += 2) {
-        DG_STEP(bf0, bf1, kb, 0);
-        if (kb + 1 < KB) DG_STEP(bf1, bf0, kb + 1, 1);
+        DG_STEP(kb, 0);
+        if (kb + 1 < KB) DG_STEP(kb + 1, 1);
     }
 #undef DG_STEP
 #undef DG_QUARTER
 #undef DG_ROWS
 #undef DG_LOAD_BF
 #undef DG_FRAG
-#undef DG_PREFETCH
 #undef DG_ISSUE_SCALES
 #undef DG_ISSUE_B
-#undef DG_ISSUE_A
+#undef DG_ISSUE_AH
+#undef DG_ISSUE_AL
+#undef DG_ISSUE_A_PART
 
     // ---- epilogue.  Lane holds tile row 16 (WAVES_M i + wm) + lr and
     // columns wcol + 16j + 4lg .. +3.  Round to bf16 (v_cvt_pk_bf16_f32:
@@ -563,17 +552,17 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 }
 
 // 256x256 tiles, 8 waves of 128x64 (two per SIMD).
-using TileLarge = TileConfig<256, 256, 2, 4, 4, false, DG_PF_DENSE>;
+using TileLarge = TileConfig<256, 256, 2, 4, 4, false>;
 // Narrower dense tiles, 8 waves of 64x112 / 64x96: fewer idle CUs in the
 // last round of tiles when N is not a good multiple of 256.
-using TileWide224 = TileConfig<256, 224, 4, 2, 4, false, 0>;
-using TileWide192 = TileConfig<256, 192, 4, 2, 4, false, 0>;
+using TileWide224 = TileConfig<256, 224, 4, 2, 4, false>;
+using TileWide192 = TileConfig<256, 192, 4, 2, 4, false>;
 // 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
 // also the dense shape for few rows.
-using TileRows128 = TileConfig<128, 256, 2, 4, 8, false, DG_PF_CONTIG>;
+using TileRows128 = TileConfig<128, 256, 2, 4, 8, false>;
 // Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
 // MFMAs of invalid rows does not shorten them.
-using TileMasked = TileConfig<256, 256, 2, 4, 4, false, DG_PF_MASKED>;
+using TileMasked = TileConfig<256, 256, 2, 4, 4, false>;
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
