@@ -14,15 +14,6 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even (the rounding of
-// the bf16 epilogue in DeepGEMM fp8_gemm.cuh).  NaN stays a quiet NaN;
-// values past the largest finite bf16 become +-inf.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 // fp32 -> OCP E4M3FN code, round to nearest even, saturated to +-448, sign
 // kept.  Normal results keep 3 of the 23 mantissa bits (carry into the
 // exponent handled by the integer add); below 2^-6 the grid step is 2^-9.

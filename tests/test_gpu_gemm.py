@@ -166,6 +166,32 @@ def test_masked_all_zero_leaves_d_untouched(orc):
     assert (got == 0xFFFF).all()
 
 
+def test_epilogue_rounding_is_exact(orc, monkeypatch):
+    """Small-integer operands and unit scales make every block sum exact in
+    fp32, so D differs from the exact value only by the bf16 rounding; many
+    sums fall on ties (odd multiples of half a bf16 step), which must round
+    to even.  Bit-exact against the oracle, every dense tile shape."""
+    rng = np.random.default_rng(257)
+    M, N, K = 256, 256, 256
+    code = {v: orc.e4m3_from_float(float(v)) for v in range(0, 9)}
+    a_val = rng.integers(0, 9, size=(M, K))
+    b_val = rng.integers(0, 9, size=(N, K))
+    qa = np.vectorize(code.get)(a_val).astype(np.uint8)
+    qb = np.vectorize(code.get)(b_val).astype(np.uint8)
+    sa = np.ones((M, K // 128), np.float32)
+    sb = np.ones((N // 128, K // 128), np.float32)
+    exact = (a_val @ b_val.T).astype(np.int64)
+    step = 2 ** (np.floor(np.log2(np.maximum(exact, 1))).astype(np.int64) - 7)
+    ties = (exact >= 256) & (exact % step == step // 2)
+    assert ties.sum() > 1000
+    ref = orc.gemm_nt(qa, sa, qb, sb)
+    case = dense_case(M, N, K, seed=0)
+    for tile in ("256x256", "256x224", "256x192", "128x256"):
+        monkeypatch.setenv("DG_FP8_DENSE_TILE", tile)
+        got = _run(case, qa, sa, qb, sb).reshape(M, N)
+        assert np.array_equal(got, ref), tile
+
+
 def test_zero_scale_block(orc):
     """A zero block of A (amax 0, scale 0) contributes nothing."""
     case = dense_case(130, 136, 512, seed=17)
