@@ -139,23 +139,48 @@ def gemm_call(case, dg, t):
 
 def time_quantize(dg, t, case, reps=20):
     """Average time of the per-token quantization of A (the activation side,
-    re-done every step in use) with HIP events; reported beside the GEMM."""
+    re-done every step in use), from fp32 and from bf16 input, with HIP
+    events; reported beside the GEMM."""
     import torch
     x = t["x_a"].reshape(-1, case.K)
+    xb = x.to(torch.bfloat16)
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.empty((x.shape[0], case.K // 128), dtype=torch.float32, device=x.device)
+
+    def timed(fn, src):
+        for _ in range(3):
+            fn(src, q, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(src, q, s)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(dg.dg_quantize_fp8_per_token, x)
+    ms_b = timed(dg.dg_quantize_fp8_per_token_bf16, xb)
+    w = t["x_b"].reshape(-1, case.K) if t["x_b"].dim() == 2 else t["x_b"][0]
+    qw = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sw = torch.empty(((w.shape[0] + 127) // 128, case.K // 128), dtype=torch.float32,
+                     device=w.device)
     for _ in range(3):
-        dg.dg_quantize_fp8_per_token(x, q, s)
+        dg.dg_quantize_fp8_per_block(w, qw, sw)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        dg.dg_quantize_fp8_per_token(x, q, s)
+        dg.dg_quantize_fp8_per_block(w, qw, sw)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms_w = e0.elapsed_time(e1) / reps
     byts = x.numel() * 5 + s.numel() * 4
+    byts_b = x.numel() * 3 + s.numel() * 4
     return {"kernel": "quantize_per_token", "rows": int(x.shape[0]), "K": case.K,
-            "us": round(ms * 1e3, 2), "GB/s": round(byts / (ms * 1e-3) / 1e9, 1)}
+            "us": round(ms * 1e3, 2), "GB/s": round(byts / (ms * 1e-3) / 1e9, 1),
+            "bf16_input_us": round(ms_b * 1e3, 2),
+            "bf16_input_GB/s": round(byts_b / (ms_b * 1e-3) / 1e9, 1),
+            "per_block_rows": int(w.shape[0]), "per_block_us": round(ms_w * 1e3, 2),
+            "per_block_GB/s": round((w.numel() * 5 + sw.numel() * 4) / (ms_w * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(case, target_s: float):

@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "DGError", "library_path", "load_library",
     "dg_fp8_gemm_nt", "dg_fp8_gemm_grouped_contiguous", "dg_fp8_gemm_grouped_masked",
-    "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_block", "dg_status_string",
+    "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16", "dg_quantize_fp8_per_block",
+    "dg_status_string",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,7 @@ def load_library():
         ("dg_fp8_gemm_grouped_contiguous", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
         ("dg_fp8_gemm_grouped_masked", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
         ("dg_quantize_fp8_per_token", [p, i64, i64, p, p, p]),
+        ("dg_quantize_fp8_per_token_bf16", [p, i64, i64, p, p, p]),
         ("dg_quantize_fp8_per_block", [p, i64, i64, p, p, p]),
     ]:
         fn = getattr(lib, name)
@@ -165,6 +167,21 @@ def dg_quantize_fp8_per_token(x, q=None, s=None):
     q = _bytes(q, "q")
     _check(q, "q", shape=(M, K)); _check(s, "s", torch.float32, (M, K // 128))
     _call("dg_quantize_fp8_per_token", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
+          _stream_ptr(x))
+    return q, s
+
+
+def dg_quantize_fp8_per_token_bf16(x, q=None, s=None):
+    """x[M][K] bf16 -> (q[M][K] uint8 e4m3 codes, s[M][K/128] fp32)."""
+    _check(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    q = _bytes(q, "q")
+    _check(q, "q", shape=(M, K)); _check(s, "s", torch.float32, (M, K // 128))
+    _call("dg_quantize_fp8_per_token_bf16", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s
 

@@ -92,6 +92,17 @@ dg_status dg_quantize_fp8_per_token(const float* x, int64_t M, int64_t K, uint8_
     return from_hip(dg::launch_quantize_per_token(x, M, K, q, s, static_cast<hipStream_t>(stream)));
 }
 
+dg_status dg_quantize_fp8_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                                         float* s, void* stream) {
+    if (K <= 0 || K % 128 != 0 || M < 0 || !product_ok(M, K)) return DG_ERR_SHAPE;
+    if (M == 0) return DG_OK;
+    const void* ptrs[] = {x, q, s};
+    dg_status st = check_ptrs(ptrs, 3);
+    if (st != DG_OK) return st;
+    return from_hip(
+        dg::launch_quantize_per_token_bf16(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
 dg_status dg_quantize_fp8_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
                                     void* stream) {
     if (K <= 0 || K % 128 != 0 || N < 0 || !product_ok(N, K)) return DG_ERR_SHAPE;

@@ -1,5 +1,5 @@
-// Device helpers shared by the gfx950 kernels of this library: number-format
-// conversions written from the formats' definitions, and MFMA operand types.
+// Device helpers shared by the gfx950 kernels of this library: vector types
+// for MFMA operands and 16-byte accesses, and the e4m3 conversion.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,22 +14,20 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// fp32 -> OCP E4M3FN code, round to nearest even, saturated to +-448, sign
-// kept.  Normal results keep 3 of the 23 mantissa bits (carry into the
-// exponent handled by the integer add); below 2^-6 the grid step is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;        // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;       // |v| >= 448
-    if (a < 0x3c800000u) {                           // |v| < 2^-6
-        float t = __uint_as_float(a) * 512.0f;       // exact power-of-two scaling
-        return sign | (uint32_t)__builtin_rintf(t);  // 0..8; 8 is the code of 2^-6
-    }
-    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-    uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-    return sign | (code > 0x7eu ? 0x7eu : code);
+// Four fp32 values -> four OCP E4M3FN codes (byte i = value i, sign kept)
+// with the hardware conversion (v_cvt_pk_fp8_f32: round to nearest even,
+// subnormal codes below 2^-6).  Inputs are clamped to +-448 first
+// (v_med3_f32), so the conversion never sees a value past the largest finite
+// e4m3: results saturate at +-448.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float a, float b, float c, float d) {
+    const float lim = 448.0f;
+    a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+    b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+    c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+    d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
 }  // namespace dg

@@ -25,6 +25,8 @@ hipError_t launch_gemm(Form form, const GemmArgs& args, hipStream_t stream);
 
 hipError_t launch_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream);
+hipError_t launch_quantize_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                                          float* s, hipStream_t stream);
 hipError_t launch_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream);
 

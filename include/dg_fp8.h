@@ -108,6 +108,13 @@ dg_status dg_fp8_gemm_grouped_masked(const uint8_t* A, const float* sa,
 dg_status dg_quantize_fp8_per_token(const float* x, int64_t M, int64_t K,
                                     uint8_t* q, float* s, void* stream);
 
+/* The same per-token quantization from bf16 activations: x [M][K] holds
+ * bf16 bit patterns (a bf16 value is exactly the fp32 value with the same
+ * upper 16 bits), converted exactly to fp32 and then quantized as above.
+ * Sizes and layout of q and s as above. */
+dg_status dg_quantize_fp8_per_token_bf16(const uint16_t* x, int64_t M, int64_t K,
+                                         uint8_t* q, float* s, void* stream);
+
 /* Per-block quantization of weights: x [N][K] fp32 -> q [N][K] and
  * s [ceil(N/128)][K/128], one scale per 128x128 block (the last row block is
  * partial when N % 128 != 0), same rounding as above.  For grouped B call it

@@ -52,6 +52,10 @@ def _load():
     lib.orc_bf16_from_double.restype = ctypes.c_uint16
     lib.orc_quantize_per_token.argtypes = [p, i64, i64, p, p]
     lib.orc_quantize_per_token.restype = None
+    lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_value.restype = ctypes.c_float
+    lib.orc_quantize_per_token_bf16.argtypes = [p, i64, i64, p, p]
+    lib.orc_quantize_per_token_bf16.restype = None
     lib.orc_quantize_per_block.argtypes = [p, i64, i64, p, p]
     lib.orc_quantize_per_block.restype = None
     lib.orc_gemm_nt.argtypes = [p, p, p, p, p, i64, i64, i64]
@@ -120,6 +124,22 @@ def quantize_per_token(x: np.ndarray):
     q = np.empty((M, K), dtype=np.uint8)
     s = np.empty((M, K // 128), dtype=np.float32)
     _load().orc_quantize_per_token(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def bf16_value(bits: int) -> float:
+    """The fp32 value of a bf16 bit pattern."""
+    return float(_load().orc_bf16_value(int(bits)))
+
+
+def quantize_per_token_bf16(x_bits: np.ndarray):
+    """x[M][K] bf16 bit patterns (uint16) -> (q[M][K] uint8, s[M][K/128] fp32)."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    assert K % 128 == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // 128), dtype=np.float32)
+    _load().orc_quantize_per_token_bf16(_ptr(x), M, K, _ptr(q), _ptr(s))
     return q, s
 
 

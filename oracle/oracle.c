@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <stdlib.h>
 #include <omp.h>
 
 /* ------------------------------------------------------------------ e4m3 */
@@ -170,6 +171,30 @@ void orc_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, fl
                 q[m * K + kb * 128 + k] = (amax == 0.0f) ? 0 : orc_e4m3_from_float(blk[k] / scale);
         }
     }
+}
+
+/* The bf16 value with bit pattern b (1 sign, 8 exponent, 7 fraction bits)
+ * is the fp32 value whose upper 16 bits are b and lower 16 bits are zero:
+ * bf16 is fp32 with the fraction cut to 7 bits, same exponent range. */
+float orc_bf16_value(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Per-token quantization of bf16 activations: each element converted
+ * exactly to fp32, then quantized as orc_quantize_per_token does. */
+void orc_quantize_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s)
+{
+    float* xf = (float*)malloc((size_t)(M * K) * sizeof(float));
+    if (!xf)
+        return;
+    for (int64_t i = 0; i < M * K; ++i)
+        xf[i] = orc_bf16_value(x[i]);
+    orc_quantize_per_token(xf, M, K, q, s);
+    free(xf);
 }
 
 /* Per-block quantization of x[N][K] into q[N][K] and s[ceil(N/128)][K/128]:

@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "dg_fp8_gemm_nt", "dg_fp8_gemm_grouped_contiguous", "dg_fp8_gemm_grouped_masked",
-        "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_block", "dg_status_string"])
+        "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16",
+        "dg_quantize_fp8_per_block", "dg_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -89,6 +90,7 @@ def test_zero_rows_is_a_no_op(lib):
     assert lib.dg_fp8_gemm_grouped_masked(None, None, None, None, None, None,
                                           3, 0, 8, 128, None) == DG_OK
     assert lib.dg_quantize_fp8_per_token(None, 0, 128, None, None, None) == DG_OK
+    assert lib.dg_quantize_fp8_per_token_bf16(None, 0, 128, None, None, None) == DG_OK
     assert lib.dg_quantize_fp8_per_block(None, 0, 128, None, None, None) == DG_OK
 
 
@@ -109,6 +111,9 @@ def test_quantize_rejections(lib):
     assert lib.dg_quantize_fp8_per_token(FAKE, 4, 100, FAKE, FAKE, None) == DG_ERR_SHAPE
     assert lib.dg_quantize_fp8_per_token(FAKE, -1, 128, FAKE, FAKE, None) == DG_ERR_SHAPE
     assert lib.dg_quantize_fp8_per_token(None, 4, 128, FAKE, FAKE, None) == DG_ERR_NULL
+    assert lib.dg_quantize_fp8_per_token_bf16(FAKE, 4, 100, FAKE, FAKE, None) == DG_ERR_SHAPE
+    assert lib.dg_quantize_fp8_per_token_bf16(FAKE, 4, 128, None, FAKE, None) == DG_ERR_NULL
+    assert lib.dg_quantize_fp8_per_token_bf16(FAKE + 2, 4, 128, FAKE, FAKE, None) == DG_ERR_ALIGN
     assert lib.dg_quantize_fp8_per_block(FAKE, 4, 128, FAKE + 1, FAKE, None) == DG_ERR_ALIGN
     assert lib.dg_quantize_fp8_per_block(FAKE, 4, 0, FAKE, FAKE, None) == DG_ERR_SHAPE
 

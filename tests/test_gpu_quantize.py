@@ -19,6 +19,15 @@ def _per_token(orc, x: np.ndarray):
     assert np.array_equal(s.cpu().numpy(), rs)
 
 
+def _per_token_bf16(orc, bits: np.ndarray):
+    xb = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, s = dg.dg_quantize_fp8_per_token_bf16(xb)
+    torch.cuda.synchronize()
+    rq, rs = orc.quantize_per_token_bf16(bits)
+    assert same_codes(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy(), rs)
+
+
 def _per_block(orc, x: np.ndarray):
     q, s = dg.dg_quantize_fp8_per_block(to_dev(x))
     torch.cuda.synchronize()
@@ -83,6 +92,21 @@ def test_quantize_workload_activations_and_weights(orc):
     case = workload("masked_16x256x7168x2048")
     _per_token(orc, case.x_a.reshape(-1, case.K)[:1024].numpy())
     _per_block(orc, case.x_b[3].numpy())
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (257, 1024), (4096, 2048)])
+def test_per_token_bf16_matches_oracle(orc, M, K):
+    x = dense_case(M, 8, K, seed=M + K + 1).x_a
+    _per_token_bf16(orc, x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_per_token_bf16_all_bit_patterns(orc):
+    """Every finite bf16 bit pattern, 128 to a block (blocks of one binade
+    and sign, so tiny and huge amax both occur)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    bits = bits[: bits.size // 128 * 128].reshape(-1, 128)
+    _per_token_bf16(orc, bits)
 
 
 def test_quantize_is_deterministic():

@@ -85,3 +85,40 @@ def test_quantize_zero_block(orc):
     assert q[1, 200] == 0xFE and s[1, 1] == np.float32(2.5) / np.float32(448.0)
     q2, s2 = orc.quantize_per_block(np.zeros((130, 128), dtype=np.float32))
     assert (s2 == 0).all() and (q2 == 0).all()
+
+
+def test_bf16_decode_pins(orc):
+    """bf16 bit patterns against their values from the format's definition
+    (1 sign, 8 exponent bits with bias 127, 7 fraction bits; exponent 0 is
+    subnormal with 2^-126 * fraction/128)."""
+    assert orc.bf16_value(0x3F80) == 1.0
+    assert orc.bf16_value(0xC000) == -2.0
+    assert orc.bf16_value(0x3EAA) == (1 + 42 / 128) * 2.0 ** -2
+    assert orc.bf16_value(0x0001) == 2.0 ** -133
+    assert orc.bf16_value(0x007F) == 127 / 128 * 2.0 ** -126
+    assert orc.bf16_value(0x7F7F) == (2 - 2.0 ** -7) * 2.0 ** 127
+    assert orc.bf16_value(0x7F80) == np.inf
+    v = orc.bf16_value(0x8000)
+    assert v == 0.0 and np.signbit(v)
+
+
+def test_per_token_bf16_worked_example(orc):
+    """One block by hand: amax 2 gives scale 2/448 = 1/224, so 1.0 -> 224
+    (code 0x76: exponent field 14, 2^(14-7) * (1 + 6/8)), -2.0 -> -448
+    (0xFE), 0.5 -> 112 (0x6E: exponent field 13), a bf16 subnormal -> 0."""
+    x = np.zeros((1, 128), dtype=np.uint16)
+    x[0, 0], x[0, 1], x[0, 2], x[0, 3] = 0x3F80, 0xC000, 0x3F00, 0x0001
+    q, s = orc.quantize_per_token_bf16(x)
+    assert s[0, 0] == np.float32(2.0) / np.float32(448.0)
+    assert list(q[0, :4]) == [0x76, 0xFE, 0x6E, 0x00]
+    assert (q[0, 4:] == 0).all()
+
+
+def test_per_token_bf16_is_fp32_path_on_decoded_values(orc):
+    rng = np.random.default_rng(16)
+    bits = rng.integers(0, 1 << 16, size=(37, 384), dtype=np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80  # no inf/NaN inputs
+    q, s = orc.quantize_per_token_bf16(bits)
+    dec = (bits.astype(np.uint32) << 16).view(np.float32)
+    q2, s2 = orc.quantize_per_token(dec)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
