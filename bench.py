@@ -77,6 +77,8 @@ def algorithmic(case):
             + groups * case.N * case.K        # B codes of groups in use
             + 4 * (rows * KB + groups * NB * KB)   # scales
             + 2 * rows * case.N)              # bf16 D
+    if case.x_c is not None:
+        byts += 4 * rows * case.N             # fp32 C
     return flop, float(byts)
 
 
@@ -125,12 +127,16 @@ def make_inputs(case, dev, dg):
         D = torch.empty((case.G, case.M, case.N), dtype=torch.bfloat16, device=dev)
     else:
         D = torch.empty((case.M, case.N), dtype=torch.bfloat16, device=dev)
-    return {"A": qa, "sa": sa, "B": qb, "sb": sb, "D": D, "aux": aux, "x_a": x_a, "x_b": x_b}
+    C = case.x_c.to(dev) if case.x_c is not None else None
+    return {"A": qa, "sa": sa, "B": qb, "sb": sb, "C": C, "D": D, "aux": aux, "x_a": x_a,
+            "x_b": x_b}
 
 
 def gemm_call(case, dg, t):
     if case.form == "dense":
         dg.dg_fp8_gemm_nt(t["A"], t["sa"], t["B"], t["sb"], t["D"])
+    elif case.form == "dense_acc":
+        dg.dg_fp8_gemm_nt_acc(t["A"], t["sa"], t["B"], t["sb"], t["C"], t["D"])
     elif case.form == "contiguous":
         dg.dg_fp8_gemm_grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
     else:
@@ -191,7 +197,7 @@ def cpu_baseline(case, target_s: float):
 
     K = case.K
     xa = case.x_a.reshape(-1, K).numpy()
-    if case.form == "dense":
+    if case.form in ("dense", "dense_acc"):
         qb, sb = oracle.quantize_per_block(case.x_b.numpy())
         routed = np.arange(case.M)
     elif case.form == "contiguous":
@@ -213,6 +219,8 @@ def cpu_baseline(case, target_s: float):
         t0 = time.perf_counter()
         if case.form == "dense":
             oracle.gemm_nt(qa, sa, qb, sb, rows=rows)
+        elif case.form == "dense_acc":
+            oracle.gemm_nt_acc(qa[rows], sa[rows], qb, sb, case.x_c.numpy()[rows])
         elif case.form == "contiguous":
             oracle.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=rows)
         else:
@@ -257,7 +265,8 @@ def main():
     base = make_inputs(case, dev, dg)
     torch.cuda.synchronize()
 
-    in_bytes = sum(base[k].numel() * base[k].element_size() for k in ("A", "sa", "B", "sb", "D"))
+    in_bytes = sum(base[k].numel() * base[k].element_size() for k in ("A", "sa", "B", "sb", "C", "D")
+                   if base[k] is not None)
     copies = max(1, -(-ROTATE_BYTES // in_bytes))
     sets = [base]
     for _ in range(copies - 1):

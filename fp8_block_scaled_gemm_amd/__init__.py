@@ -23,7 +23,8 @@ import torch
 
 __all__ = [
     "DGError", "library_path", "load_library",
-    "dg_fp8_gemm_nt", "dg_fp8_gemm_grouped_contiguous", "dg_fp8_gemm_grouped_masked",
+    "dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_fp8_gemm_grouped_contiguous",
+    "dg_fp8_gemm_grouped_masked",
     "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16", "dg_quantize_fp8_per_block",
     "dg_status_string",
 ]
@@ -57,6 +58,7 @@ def load_library():
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     for name, args in [
         ("dg_fp8_gemm_nt", [p, p, p, p, p, i64, i64, i64, p]),
+        ("dg_fp8_gemm_nt_acc", [p, p, p, p, p, p, i64, i64, i64, p]),
         ("dg_fp8_gemm_grouped_contiguous", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
         ("dg_fp8_gemm_grouped_masked", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
         ("dg_quantize_fp8_per_token", [p, i64, i64, p, p, p]),
@@ -121,6 +123,21 @@ def dg_fp8_gemm_nt(A, sa, B, sb, D):
     _check(D, "D", _D_TYPES, (M, N))
     _call("dg_fp8_gemm_nt", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
           D.data_ptr(), M, N, K, _stream_ptr(D))
+    return D
+
+
+def dg_fp8_gemm_nt_acc(A, sa, B, sb, C, D):
+    """Dense with an fp32 addend: D[M][N] = bf16(C + the dense sum)."""
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    KB, NB = K // 128, (N + 127) // 128
+    _check(A, "A"); _check(B, "B", shape=(N, K))
+    _check(sa, "sa", torch.float32, (M, KB)); _check(sb, "sb", torch.float32, (NB, KB))
+    _check(C, "C", torch.float32, (M, N))
+    _check(D, "D", _D_TYPES, (M, N))
+    _call("dg_fp8_gemm_nt_acc", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+          C.data_ptr(), D.data_ptr(), M, N, K, _stream_ptr(D))
     return D
 
 

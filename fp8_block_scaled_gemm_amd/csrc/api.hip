@@ -50,6 +50,20 @@ dg_status dg_fp8_gemm_nt(const uint8_t* A, const float* sa, const uint8_t* B, co
     return from_hip(dg::launch_gemm(dg::Form::Dense, a, static_cast<hipStream_t>(stream)));
 }
 
+dg_status dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                             const float* C, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                             void* stream) {
+    dg_status s = check_nk(N, K);
+    if (s != DG_OK) return s;
+    if (M < 0 || !product_ok(M, K) || !product_ok(M, N) || M > 0x7fffffffLL) return DG_ERR_SHAPE;
+    if (N >= (1LL << 22)) return DG_ERR_SHAPE;  // 256 rows of fp32 C within 32-bit offsets
+    if (M == 0) return DG_OK;
+    const void* ptrs[] = {A, sa, B, sb, C, D};
+    if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
+    dg::GemmArgs a{A, sa, B, sb, D, nullptr, M, N, K, 1, C};
+    return from_hip(dg::launch_gemm(dg::Form::DenseAcc, a, static_cast<hipStream_t>(stream)));
+}
+
 dg_status dg_fp8_gemm_grouped_contiguous(const uint8_t* A, const float* sa, const uint8_t* B,
                                          const float* sb, uint16_t* D,
                                          const int32_t* grouped_layout, int64_t M_sum, int64_t N,

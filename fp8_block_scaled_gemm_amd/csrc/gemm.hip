@@ -248,7 +248,7 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
     const int in_span = tile % span;
     ti.m0 = (first_m + in_span % gm) * T::BM;
     ti.n0 = (in_span / gm) * T::BN;
-    if (kForm == Form::Dense) {
+    if (kForm == Form::Dense || kForm == Form::DenseAcc) {
         ti.valid = (int)min<int64_t>(T::BM, rows - ti.m0);
         ti.arow0 = ti.m0;
     } else {
@@ -286,7 +286,8 @@ template <class T, Form kForm>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
     const float* __restrict__ sb, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
-    int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks, int n_blocks) {
+    const float* __restrict__ C, int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks,
+    int n_blocks) {
     // Two A stages then two B stages (after the K loop: the bf16 output tile).
     // Scales come in chunks of four K blocks, two chunk buffers: row scales
     // as [row][4], column-block scales as [block][4].
@@ -492,41 +493,75 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 #undef DG_ISSUE_A_PART
 
     // ---- epilogue.  Lane holds tile row 16 (WAVES_M i + wm) + lr and
-    // columns wcol + 16j + 4lg .. +3.  Round to bf16 (v_cvt_pk_bf16_f32:
-    // nearest even), stage the whole tile in LDS, then write it back in full
-    // 16-byte chunks, consecutive lanes on consecutive chunks of a row.  In
-    // LDS (row pitch kPitchChunks chunks), 16-byte chunk c of row r sits at
-    // c ^ (r & 15): the 16 rows a fragment store touches land in distinct banks.
-    constexpr int kRowBytes = T::kPitchChunks * 16;
-    constexpr int kChunks = T::BN / 8;  // 16-byte chunks of an output row
+    // columns wcol + 16j + 4lg .. +3.
     wait_vmcnt<0>();  // the empty loads of the last steps have retired
     lds_barrier();
-    uint8_t* const sD = smem;
+    if constexpr (kForm == Form::DenseAcc) {
+        // D = bf16(C + acc): C is read straight into the accumulators'
+        // layout (one 16-byte load per sub-tile and lane), half of the
+        // wave's sub-tile rows at a time with all of that half's loads in
+        // flight, and added in fp32 before the single rounding below.  The
+        // buffer ends with the tile's last valid row: rows past it read as
+        // zero; columns past N of a valid row read C values of the next row
+        // (or zero after the last one) and are never stored.
+        const float* const tileC = C + ti.arow0 * N + ti.n0;
+        const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(tileC), (short)0,
+            (int)(uint32_t)(((int64_t)(ti.valid - 1) * N + (N - ti.n0)) * 4), 0x00020000);
+        constexpr int kH = T::TM / 2;
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-        const int row = 16 * (T::WAVES_M * i + wm) + lr;
+        for (int h = 0; h < 2; ++h) {
+            v4f c[kH][T::TN];
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const int col = wcol + 16 * j + 4 * lg;
-            const v2f lo = {acc[i][j][0], acc[i][j][1]};
-            const v2f hi = {acc[i][j][2], acc[i][j][3]};
-            v2u packed;
-            packed[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2bf));
-            packed[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2bf));
-            *reinterpret_cast<v2u*>(sD + row * kRowBytes + (((col >> 3) ^ (row & 15)) << 4) +
-                                    ((col >> 2) & 1) * 8) = packed;
+            for (int ii = 0; ii < kH; ++ii) {
+                const int row = 16 * (T::WAVES_M * (h * kH + ii) + wm) + lr;
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) {
+                    const uint32_t off = ((uint32_t)row * (uint32_t)N + wcol + 16 * j + 4 * lg) * 4u;
+                    c[ii][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < kH; ++ii)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) acc[h * kH + ii][j] += c[ii][j];
         }
     }
-    __syncthreads();
-    static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
+    {
+        // Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage the whole
+        // tile in LDS, then write it back in full 16-byte chunks, consecutive
+        // lanes on consecutive chunks of a row.  In LDS (row pitch
+        // kPitchChunks chunks), 16-byte chunk c of row r sits at c ^ (r & 15):
+        // the 16 rows a fragment store touches land in distinct banks.
+        constexpr int kRowBytes = T::kPitchChunks * 16;
+        constexpr int kChunks = T::BN / 8;  // 16-byte chunks of an output row
+        uint8_t* const sD = smem;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int row = 16 * (T::WAVES_M * i + wm) + lr;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int col = wcol + 16 * j + 4 * lg;
+                const v2f lo = {acc[i][j][0], acc[i][j][1]};
+                const v2f hi = {acc[i][j][2], acc[i][j][3]};
+                v2u packed;
+                packed[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2bf));
+                packed[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2bf));
+                *reinterpret_cast<v2u*>(sD + row * kRowBytes + (((col >> 3) ^ (row & 15)) << 4) +
+                                        ((col >> 2) & 1) * 8) = packed;
+            }
+        }
+        __syncthreads();
+        static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
 #pragma unroll 4
-    for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
-        const int row = q / kChunks, c = q % kChunks;
-        const int64_t col = ti.n0 + c * 8;
-        bool ok = row < ti.valid && col < N;
-        if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
-        const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
-        if (ok) *reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col) = v;
+        for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
+            const int row = q / kChunks, c = q % kChunks;
+            const int64_t col = ti.n0 + c * 8;
+            bool ok = row < ti.valid && col < N;
+            if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
+            const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
+            if (ok) *reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col) = v;
+        }
     }
 }
 
@@ -545,8 +580,11 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     // per-lane 32-bit offsets: a tile's rows of K bytes, its A scales
     if ((int64_t)std::max(T::BM, T::BN) * a.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    // and a tile's rows of fp32 C
+    if (kForm == Form::DenseAcc && (int64_t)T::BM * a.N * 4 >= (int64_t(1) << 32))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<T, kForm>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
-                       a.A, a.sa, a.B, a.sb, a.D, a.aux, a.rows, a.N, a.K, a.G, (int)m_blocks,
+                       a.A, a.sa, a.B, a.sb, a.D, a.aux, a.C, a.rows, a.N, a.K, a.G, (int)m_blocks,
                        (int)n_blocks);
     return hipGetLastError();
 }
@@ -593,15 +631,20 @@ static int forced_dense_shape() {
 // ceil(tiles / CUs) rounds of one tile's time.  A tile's time scales with its
 // area times a per-shape cost per output element (narrower tiles re-read
 // more fragments per MFMA); pick the shape with the least estimated time.
-hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
+template <Form kForm>
+static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     struct Shape { int bm, bn; double rel; };
     static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.05}, {256, 192, 1.10},
                                     {128, 256, 1.15}};
+    // the accumulating epilogue stages fp32 rows of a power-of-two width
+    const bool acc = kForm == Form::DenseAcc;
     const int64_t cus = device_cus();
     int best = forced_dense_shape();
+    if (acc && (best == 1 || best == 2)) best = -1;
     if (best < 0) {
         double best_cost = 0;
         for (int i = 0; i < 4; ++i) {
+            if (acc && (i == 1 || i == 2)) continue;
             const Shape& sh = kShapes[i];
             const int64_t tiles = ((a.rows + sh.bm - 1) / sh.bm) * ((a.N + sh.bn - 1) / sh.bn);
             const double cost = (double)((tiles + cus - 1) / cus) * sh.bm * sh.bn * sh.rel;
@@ -611,17 +654,23 @@ hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
             }
         }
     }
-    switch (best) {
-        case 1: return launch_tiled<TileWide224, Form::Dense>(a, stream);
-        case 2: return launch_tiled<TileWide192, Form::Dense>(a, stream);
-        case 3: return launch_tiled<TileRows128, Form::Dense>(a, stream);
-        default: return launch_tiled<TileLarge, Form::Dense>(a, stream);
+    if constexpr (kForm == Form::DenseAcc) {
+        if (best == 3) return launch_tiled<TileRows128, kForm>(a, stream);
+        return launch_tiled<TileLarge, kForm>(a, stream);
+    } else {
+        switch (best) {
+            case 1: return launch_tiled<TileWide224, kForm>(a, stream);
+            case 2: return launch_tiled<TileWide192, kForm>(a, stream);
+            case 3: return launch_tiled<TileRows128, kForm>(a, stream);
+            default: return launch_tiled<TileLarge, kForm>(a, stream);
+        }
     }
 }
 
 hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
     switch (form) {
-        case Form::Dense: return launch_dense(a, stream);
+        case Form::Dense: return launch_dense<Form::Dense>(a, stream);
+        case Form::DenseAcc: return launch_dense<Form::DenseAcc>(a, stream);
         case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous>(a, stream);
         case Form::Masked: return launch_tiled<TileMasked, Form::Masked>(a, stream);
     }

@@ -8,7 +8,8 @@
 
 namespace dg {
 
-enum class Form : int { Dense = 0, Contiguous = 1, Masked = 2 };
+// DenseAcc: dense routing, D = bf16(C + A B^T scaled) with C fp32 [rows][N]
+enum class Form : int { Dense = 0, Contiguous = 1, Masked = 2, DenseAcc = 3 };
 
 struct GemmArgs {
     const uint8_t* A;     // e4m3 codes, K-contiguous rows
@@ -19,6 +20,7 @@ struct GemmArgs {
     const int32_t* aux;   // contiguous: group id per row; masked: valid rows per group
     int64_t rows;         // dense: M; contiguous: M_sum; masked: M_max (rows per slab)
     int64_t N, K, G;
+    const float* C;       // DenseAcc: fp32 [rows][N] added before the bf16 rounding
 };
 
 hipError_t launch_gemm(Form form, const GemmArgs& args, hipStream_t stream);

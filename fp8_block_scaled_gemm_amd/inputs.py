@@ -25,12 +25,13 @@ import torch
 class Case:
     """One synthetic workload.
 
-    form: "dense", "contiguous" or "masked".
+    form: "dense", "dense_acc", "contiguous" or "masked".
     x_a:  fp32 activations, [M][K] (dense), [M_sum][K] (contiguous) or
           [G][M_max][K] (masked).
     x_b:  fp32 weights, [N][K] (dense) or [G][N][K] (grouped).
     layout: int32 [M_sum] group id per row, -1 on padding (contiguous).
     masked_m: int32 [G] valid rows per group (masked).
+    x_c:  fp32 addend [M][N] (dense_acc).
     """
     name: str
     form: str
@@ -43,10 +44,11 @@ class Case:
     layout: torch.Tensor | None = None
     masked_m: torch.Tensor | None = None
     group_rows: list = field(default_factory=list)
+    x_c: torch.Tensor | None = None
 
     @property
     def valid_rows(self) -> int:
-        if self.form == "dense":
+        if self.form in ("dense", "dense_acc"):
             return self.M
         if self.form == "contiguous":
             return int((self.layout >= 0).sum())
@@ -54,7 +56,7 @@ class Case:
 
     @property
     def active_groups(self) -> int:
-        if self.form == "dense":
+        if self.form in ("dense", "dense_acc"):
             return 1
         if self.form == "contiguous":
             return int(torch.unique(self.layout[self.layout >= 0]).numel())
@@ -72,6 +74,16 @@ def dense_case(M: int, N: int, K: int, seed: int, name: str = "dense") -> Case:
     x_a = torch.randn(M, K, generator=g, dtype=torch.float32)
     x_b = torch.randn(N, K, generator=g, dtype=torch.float32)
     return Case(name, "dense", M, N, K, 1, x_a, x_b)
+
+
+def dense_acc_case(M: int, N: int, K: int, seed: int, name: str = "dense_acc") -> Case:
+    """Dense operands plus an fp32 addend C of the product's magnitude
+    (standard normal times sqrt(K))."""
+    g = _gen(seed)
+    x_a = torch.randn(M, K, generator=g, dtype=torch.float32)
+    x_b = torch.randn(N, K, generator=g, dtype=torch.float32)
+    x_c = torch.randn(M, N, generator=g, dtype=torch.float32) * float(K) ** 0.5
+    return Case(name, "dense_acc", M, N, K, 1, x_a, x_b, x_c=x_c)
 
 
 def contiguous_case(G: int, N: int, K: int, seed: int, m_lo: int = 3072, m_hi: int = 5120,
@@ -118,6 +130,8 @@ WORKLOADS = {
     "dense_128x7168x2048": lambda: dense_case(128, 7168, 2048, 22, "dense_128x7168x2048"),
     "dense_4096x24576x1536": lambda: dense_case(4096, 24576, 1536, 3, "dense_4096x24576x1536"),
     "dense_4096x2112x7168": lambda: dense_case(4096, 2112, 7168, 31, "dense_4096x2112x7168"),
+    "dense_acc_4096x7168x2048": lambda: dense_acc_case(4096, 7168, 2048, 23,
+                                                       "dense_acc_4096x7168x2048"),
     "contiguous_8x4096x7168": lambda: contiguous_case(8, 4096, 7168, 4, name="contiguous_8x4096x7168"),
     "masked_16x256x4096x7168": lambda: masked_case(16, 256, 4096, 7168, 5, name="masked_16x256x4096x7168"),
     "masked_16x256x7168x2048": lambda: masked_case(16, 256, 7168, 2048, 51, name="masked_16x256x7168x2048"),

@@ -66,6 +66,19 @@ dg_status dg_fp8_gemm_nt(const uint8_t* A, const float* sa,
                          uint16_t* D, int64_t M, int64_t N, int64_t K,
                          void* stream);
 
+/* Dense form with an fp32 addend: D = bf16(C + the dense form's sum), C
+ * added before the single rounding to bf16.  The accumulate case of the
+ * Triton Gluon tutorial page "TCGen05 Copy Instruction" (its matmul
+ * accumulate section: D = A @ B + C with C held in fp32), applied to the
+ * block-scaled product.
+ *   C  [M][N]  fp32 (input, not modified), other arguments as in
+ *   dg_fp8_gemm_nt; C and D must not overlap.  Same size rules, and
+ *   N < 2^22 (DG_ERR_SHAPE otherwise). */
+dg_status dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sa,
+                             const uint8_t* B, const float* sb,
+                             const float* C, uint16_t* D,
+                             int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Contiguous-grouped form (MoE experts with rows sorted by expert).
  *   A  [M_sum][K]  e4m3         sa [M_sum][K/128]               fp32
  *   B  [G][N][K]   e4m3         sb [G][ceil(N/128)][K/128]      fp32

@@ -60,6 +60,8 @@ def _load():
     lib.orc_quantize_per_block.restype = None
     lib.orc_gemm_nt.argtypes = [p, p, p, p, p, i64, i64, i64]
     lib.orc_gemm_nt.restype = None
+    lib.orc_gemm_nt_acc.argtypes = [p, p, p, p, p, p, i64, i64, i64]
+    lib.orc_gemm_nt_acc.restype = None
     lib.orc_gemm_nt_rows.argtypes = [p, p, p, p, i64, i64, i64, p, i64, p]
     lib.orc_gemm_nt_rows.restype = None
     lib.orc_gemm_grouped_contiguous.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64]
@@ -181,6 +183,20 @@ def gemm_nt(A, sa, B, sb, D=None, rows=None):
     lib.orc_gemm_nt(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K)
     return D
 
+
+
+def gemm_nt_acc(A, sa, B, sb, C):
+    """Dense form with an fp32 addend: D = bf16(C + the dense sum), C[M][N]
+    fp32 joining the fp64 sum before the single rounding."""
+    A = _c(A, np.uint8); sa = _c(sa, np.float32); B = _c(B, np.uint8); sb = _c(sb, np.float32)
+    C = _c(C, np.float32)
+    M, K = A.shape
+    N = B.shape[0]
+    assert K % 128 == 0 and B.shape[1] == K and C.shape == (M, N)
+    assert sa.shape == (M, K // 128) and sb.shape == ((N + 127) // 128, K // 128)
+    D = np.full((M, N), 0xFFFF, dtype=np.uint16)
+    _load().orc_gemm_nt_acc(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(C), _ptr(D), M, N, K)
+    return D
 
 def gemm_grouped_contiguous(A, sa, B, sb, layout, D=None, rows=None):
     """Contiguous-grouped form.  A[M_sum][K], sa[M_sum][K/128],

@@ -234,9 +234,9 @@ void orc_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, fl
  *   a_row : K codes of one A row      sa_row : K/128 scales of that row
  *   b     : [N][K] codes              sb     : [ceil(N/128)][K/128] scales
  *   d_row : N bf16 outputs                                                 */
-static void oracle_row(const uint8_t* a_row, const float* sa_row,
-                       const uint8_t* b, const float* sb,
-                       int64_t N, int64_t K, uint16_t* d_row)
+static void oracle_row_c(const uint8_t* a_row, const float* sa_row,
+                         const uint8_t* b, const float* sb, const float* c_row,
+                         int64_t N, int64_t K, uint16_t* d_row)
 {
     double dec[256];
     for (int c = 0; c < 256; ++c)
@@ -253,8 +253,17 @@ static void oracle_row(const uint8_t* a_row, const float* sa_row,
             double scale = (double)sa_row[kb] * (double)sb_row[kb];
             v += scale * block;
         }
+        if (c_row)
+            v += (double)c_row[n];
         d_row[n] = orc_bf16_from_double(v);
     }
+}
+
+static void oracle_row(const uint8_t* a_row, const float* sa_row,
+                       const uint8_t* b, const float* sb,
+                       int64_t N, int64_t K, uint16_t* d_row)
+{
+    oracle_row_c(a_row, sa_row, b, sb, NULL, N, K, d_row);
 }
 
 /* Dense form: A[M][K], sa[M][K/128], B[N][K], sb[ceil(N/128)][K/128],
@@ -266,6 +275,19 @@ void orc_gemm_nt(const uint8_t* A, const float* sa, const uint8_t* B, const floa
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; ++m)
         oracle_row(A + m * K, sa + m * KB, B, sb, N, K, D + m * N);
+}
+
+/* Dense form with an fp32 addend C[M][N]: D = bf16(C + the dense sum),
+ * the addend joining the fp64 sum before the single rounding (the matmul
+ * accumulate case of the Triton Gluon tutorial page "TCGen05 Copy
+ * Instruction": D = A @ B + C with C in fp32). */
+void orc_gemm_nt_acc(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                     const float* C, uint16_t* D, int64_t M, int64_t N, int64_t K)
+{
+    int64_t KB = K / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        oracle_row_c(A + m * K, sa + m * KB, B, sb, C + m * N, N, K, D + m * N);
 }
 
 /* Dense form on a chosen list of rows; row i of out[nrows][N] receives

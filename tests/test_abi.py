@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "dg_fp8_gemm_nt", "dg_fp8_gemm_grouped_contiguous", "dg_fp8_gemm_grouped_masked",
-        "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16",
+        "dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_fp8_gemm_grouped_contiguous",
+        "dg_fp8_gemm_grouped_masked", "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16",
         "dg_quantize_fp8_per_block", "dg_status_string"])
 
 
@@ -92,6 +92,16 @@ def test_zero_rows_is_a_no_op(lib):
     assert lib.dg_quantize_fp8_per_token(None, 0, 128, None, None, None) == DG_OK
     assert lib.dg_quantize_fp8_per_token_bf16(None, 0, 128, None, None, None) == DG_OK
     assert lib.dg_quantize_fp8_per_block(None, 0, 128, None, None, None) == DG_OK
+
+
+def test_acc_rejections(lib):
+    f = lib.dg_fp8_gemm_nt_acc
+    assert f(None, None, None, None, None, None, 0, 8, 128, None) == DG_OK          # M = 0
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 8, 128, None) == DG_ERR_NULL     # C
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 4, 8, 128, None) == DG_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 128, None) == DG_ERR_SHAPE  # N % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 100, None) == DG_ERR_SHAPE   # K % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1 << 22, 128, None) == DG_ERR_SHAPE  # N
 
 
 def test_grouped_rejections(lib):

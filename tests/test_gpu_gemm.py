@@ -41,6 +41,9 @@ def _run(case, qa, sa, qb, sb):
     if case.form == "dense":
         D = torch.full((case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
         dg.dg_fp8_gemm_nt(A, SA, B, SB, D)
+    elif case.form == "dense_acc":
+        D = torch.full((case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
+        dg.dg_fp8_gemm_nt_acc(A, SA, B, SB, to_dev(case.x_c.numpy()), D)
     elif case.form == "contiguous":
         D = torch.full((case.M, case.N), SENTINEL, dtype=torch.int16, device=A.device)
         dg.dg_fp8_gemm_grouped_contiguous(A, SA, B, SB, D, to_dev(case.layout.numpy()))
@@ -54,6 +57,8 @@ def _run(case, qa, sa, qb, sb):
 def _oracle_full(orc, case, qa, sa, qb, sb):
     if case.form == "dense":
         return orc.gemm_nt(qa, sa, qb, sb)
+    if case.form == "dense_acc":
+        return orc.gemm_nt_acc(qa, sa, qb, sb, case.x_c.numpy())
     if case.form == "contiguous":
         return orc.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy())
     return orc.gemm_grouped_masked(qa, sa, qb, sb, case.masked_m.numpy())
@@ -61,7 +66,7 @@ def _oracle_full(orc, case, qa, sa, qb, sb):
 
 def _routed_rows(case) -> np.ndarray:
     """Flat row indices (into D viewed as [rows][N]) the call must write."""
-    if case.form == "dense":
+    if case.form in ("dense", "dense_acc"):
         return np.arange(case.M)
     if case.form == "contiguous":
         lay = case.layout.numpy()
@@ -192,6 +197,27 @@ def test_epilogue_rounding_is_exact(orc, monkeypatch):
         assert np.array_equal(got, ref), tile
 
 
+@pytest.mark.parametrize("tile", ["256x256", "128x256", None])
+@pytest.mark.parametrize("M,N,K", [(300, 488, 384), (64, 256, 128), (512, 520, 256)])
+def test_dense_acc_parity(orc, monkeypatch, tile, M, N, K):
+    """D = bf16(C + dense sum) against the oracle; C of the product's size
+    and, in every other row, a hundred times larger (a dropped or doubled
+    addend fails)."""
+    if tile:
+        monkeypatch.setenv("DG_FP8_DENSE_TILE", tile)
+    case = dense_case(M, N, K, seed=M * 7 + N + K)
+    qa, sa, qb, sb = _prepared(orc, case)
+    rng = np.random.default_rng(M + N)
+    C = (rng.standard_normal((M, N)) * np.where(np.arange(M)[:, None] % 2, 100.0, 1.0)
+         * np.sqrt(K)).astype(np.float32)
+    D = torch.full((M, N), SENTINEL, dtype=torch.int16, device="cuda")
+    dg.dg_fp8_gemm_nt_acc(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), to_dev(C), D)
+    torch.cuda.synchronize()
+    got = D.cpu().numpy().view(np.uint16)
+    ref = orc.gemm_nt_acc(qa, sa, qb, sb, C)
+    assert_close_bf16(got, ref, f"acc {M}x{N}x{K} {tile}")
+
+
 def test_zero_scale_block(orc):
     """A zero block of A (amax 0, scale 0) contributes nothing."""
     case = dense_case(130, 136, 512, seed=17)
@@ -212,7 +238,8 @@ def test_gemm_is_deterministic(orc):
 
 FULL = ["dense_128x512x512", "dense_4096x7168x2048", "dense_64x7168x2048",
         "dense_128x7168x2048", "dense_4096x24576x1536", "dense_4096x2112x7168",
-        "contiguous_8x4096x7168", "masked_16x256x4096x7168", "masked_16x256x7168x2048"]
+        "dense_acc_4096x7168x2048", "contiguous_8x4096x7168", "masked_16x256x4096x7168",
+        "masked_16x256x7168x2048"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -228,6 +255,8 @@ def test_full_size_sampled_rows(orc, name):
                                      rng.choice(routed, size=min(12, routed.size), replace=False)]))
     if case.form == "dense":
         ref = orc.gemm_nt(qa, sa, qb, sb, rows=pick)
+    elif case.form == "dense_acc":
+        ref = orc.gemm_nt_acc(qa[pick], sa[pick], qb, sb, case.x_c.numpy()[pick])
     elif case.form == "contiguous":
         ref = orc.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=pick)
     else:

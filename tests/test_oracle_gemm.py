@@ -261,3 +261,63 @@ def test_untouched_rows_keep_prefill(orc):
     orc.gemm_grouped_contiguous(np.zeros((128, K), np.uint8), np.ones((128, 1), np.float32),
                                 B, sb, lay, D=D2)
     assert (D2 == 0x4321).all()
+
+
+# ---------------------------------------------------------------- accumulate
+def test_acc_with_zero_addend_is_the_dense_form(orc):
+    A = e4m3_pattern_matrix(12, 256, 31)
+    B = e4m3_pattern_matrix(40, 256, 32)
+    rng = np.random.default_rng(33)
+    sa = rng.uniform(0.5, 2, (12, 2)).astype(np.float32)
+    sb = rng.uniform(0.5, 2, (1, 2)).astype(np.float32)
+    C = np.zeros((12, 40), np.float32)
+    assert np.array_equal(orc.gemm_nt_acc(A, sa, B, sb, C), orc.gemm_nt(A, sa, B, sb))
+
+
+def test_acc_with_zero_product_rounds_the_addend(orc):
+    """A = 0: D is C rounded to bf16 (torch's fp32 -> bf16 cast, nearest even)."""
+    rng = np.random.default_rng(34)
+    C = (rng.standard_normal((9, 24)) * 10.0 ** rng.integers(-30, 30, (9, 24))).astype(np.float32)
+    A = np.zeros((9, 128), np.uint8)
+    B = e4m3_pattern_matrix(24, 128, 35)
+    D = orc.gemm_nt_acc(A, np.ones((9, 1), np.float32), B, np.ones((1, 1), np.float32), C)
+    ref = torch.from_numpy(C).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(D, ref)
+
+
+def test_acc_exact_integer_case(orc):
+    """Small integers in A, B and C with unit scales: D equals the int64
+    matmul plus C exactly while |V + C| <= 256."""
+    rng = np.random.default_rng(36)
+    M, N, K = 16, 24, 128
+    ia = rng.integers(-3, 4, (M, K)); ib = rng.integers(-3, 4, (N, K))
+    mask = np.zeros((M, K), bool)
+    for m in range(M):
+        mask[m, rng.choice(K, 8, replace=False)] = True
+    ia = np.where(mask, ia, 0)
+    ic = rng.integers(-150, 151, (M, N))
+    to_code = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    D = orc.gemm_nt_acc(to_code(ia), np.ones((M, 1), np.float32), to_code(ib),
+                        np.ones((1, 1), np.float32), ic.astype(np.float32))
+    V = ia.astype(np.int64) @ ib.astype(np.int64).T + ic
+    assert np.abs(V).max() <= 256
+    assert np.array_equal(bf16_to_f64(D), V.astype(np.float64))
+
+
+def test_acc_brute_force_rational(orc):
+    """Exact rational sum plus C, rounded once, against the oracle."""
+    rng = np.random.default_rng(37)
+    M, N, K = 3, 5, 256
+    A = e4m3_pattern_matrix(M, K, 38); B = e4m3_pattern_matrix(N, K, 39)
+    sa = rng.uniform(0.1, 3, (M, 2)).astype(np.float32)
+    sb = rng.uniform(0.1, 3, (1, 2)).astype(np.float32)
+    C = (rng.standard_normal((M, N)) * 50).astype(np.float32)
+    D = orc.gemm_nt_acc(A, sa, B, sb, C)
+    da, db = dec(A), dec(B)
+    for m in range(M):
+        for n in range(N):
+            v = Fraction(float(C[m, n]))
+            for k in range(K):
+                s = Fraction(float(sa[m, k // 128])) * Fraction(float(sb[0, k // 128]))
+                v += s * Fraction(da[m, k]) * Fraction(db[n, k])
+            assert D[m, n] == bf16_bits_of_fraction(v), (m, n)
