@@ -58,6 +58,14 @@ def _load():
     lib.orc_quantize_per_token_bf16.restype = None
     lib.orc_quantize_per_block.argtypes = [p, i64, i64, p, p]
     lib.orc_quantize_per_block.restype = None
+    lib.orc_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0_value.restype = ctypes.c_double
+    lib.orc_e8m0_exponent.argtypes = [ctypes.c_float]
+    lib.orc_e8m0_exponent.restype = ctypes.c_int
+    lib.orc_quantize_per_token_e8m0.argtypes = [p, i64, i64, p, p]
+    lib.orc_quantize_per_token_e8m0.restype = None
+    lib.orc_quantize_per_block_e8m0.argtypes = [p, i64, i64, p, p]
+    lib.orc_quantize_per_block_e8m0.restype = None
     lib.orc_gemm_nt.argtypes = [p, p, p, p, p, i64, i64, i64]
     lib.orc_gemm_nt.restype = None
     lib.orc_gemm_nt_acc.argtypes = [p, p, p, p, p, p, i64, i64, i64]
@@ -154,6 +162,78 @@ def quantize_per_block(x: np.ndarray):
     s = np.empty(((N + 127) // 128, K // 128), dtype=np.float32)
     _load().orc_quantize_per_block(_ptr(x), N, K, _ptr(q), _ptr(s))
     return q, s
+
+
+# ------------------------------------------------------ power-of-two scales
+
+def e8m0_pitch(kb: int) -> int:
+    """Bytes per row of exponent scales: K/128 rounded up to a multiple of 4."""
+    return (kb + 3) // 4 * 4
+
+
+def e8m0_value(b: int) -> float:
+    """2^(b - 127) for an E8M0 byte b; NaN for 255."""
+    return float(_load().orc_e8m0_value(int(b) & 0xFF))
+
+
+def e8m0_exponent(amax: float) -> int:
+    """Smallest e >= -127 with amax <= 448 * 2^e (amax taken as fp32)."""
+    return int(_load().orc_e8m0_exponent(float(np.float32(amax))))
+
+
+def e8m0_decode(s: np.ndarray) -> np.ndarray:
+    """fp32 values of E8M0 bytes (exact: 2^-127 is an fp32 subnormal), with
+    the 256 values taken from the C decode above."""
+    table = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64).astype(np.float32)
+    return table[np.asarray(s, dtype=np.uint8)]
+
+
+def quantize_per_token_e8m0(x: np.ndarray):
+    """x[M][K] fp32 -> (q[M][K] uint8 codes, s[M][KBp] uint8 exponents);
+    padding bytes of s are zero."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    assert K % 128 == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.zeros((M, e8m0_pitch(K // 128)), dtype=np.uint8)
+    _load().orc_quantize_per_token_e8m0(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_per_block_e8m0(x: np.ndarray):
+    """x[N][K] fp32 -> (q[N][K] uint8, s[ceil(N/128)][KBp] uint8 exponents)."""
+    x = _c(x, np.float32)
+    N, K = x.shape
+    assert K % 128 == 0
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.zeros(((N + 127) // 128, e8m0_pitch(K // 128)), dtype=np.uint8)
+    _load().orc_quantize_per_block_e8m0(_ptr(x), N, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def _e8m0_scales(s: np.ndarray, KB: int) -> np.ndarray:
+    return np.ascontiguousarray(e8m0_decode(np.asarray(s)[..., :KB]))
+
+
+def gemm_nt_e8m0(A, sa, B, sb, rows=None):
+    """Dense form with exponent-byte scales sa[M][KBp], sb[ceil(N/128)][KBp]:
+    the definition of gemm_nt with sa, sb replaced by their powers of two."""
+    KB = A.shape[-1] // 128
+    return gemm_nt(A, _e8m0_scales(sa, KB), B, _e8m0_scales(sb, KB), rows=rows)
+
+
+def gemm_grouped_contiguous_e8m0(A, sa, B, sb, layout, rows=None):
+    """Contiguous-grouped form with exponent-byte scales."""
+    KB = A.shape[-1] // 128
+    return gemm_grouped_contiguous(A, _e8m0_scales(sa, KB), B, _e8m0_scales(sb, KB), layout,
+                                   rows=rows)
+
+
+def gemm_grouped_masked_e8m0(A, sa, B, sb, masked_m, rows=None):
+    """Masked-grouped form with exponent-byte scales."""
+    KB = A.shape[-1] // 128
+    return gemm_grouped_masked(A, _e8m0_scales(sa, KB), B, _e8m0_scales(sb, KB), masked_m,
+                               rows=rows)
 
 
 # -------------------------------------------------------------------- GEMM

@@ -225,6 +225,96 @@ void orc_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, fl
     }
 }
 
+/* --------------------------------------------------- power-of-two scales */
+
+/* Power-of-two (E8M0) block scales for the hardware block-scaled matrix
+ * instruction (the Gluon tutorial page "TCGen05 Copy Instruction", its
+ * section on tensor scales: per-block scales are handed to the scaled MMA
+ * next to the operands and applied by it).  Byte b stands for 2^(b - 127);
+ * 255 is NaN.  The recipe is not on the pages; the reading taken here keeps
+ * the 1x128 / 128x128 blocks of the fp32 recipe and rounds the scale up to
+ * a power of two: a block's exponent is the smallest e >= -127 with
+ * amax <= 448 * 2^e, so x * 2^-e stays within the e4m3 range and no code
+ * saturates.  Scales are stored one byte per block, rows of K/128 bytes
+ * padded to a multiple of 4 (the padding is neither read nor written). */
+double orc_e8m0_value(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* The exponent of the rule above, found by counting up from -127: plain and
+ * slow, at most 248 steps for a finite amax. */
+int orc_e8m0_exponent(float amax)
+{
+    int e = -127;
+    while ((double)amax > ldexp(448.0, e))
+        ++e;
+    return e;
+}
+
+/* Codes of one block: e4m3 of x * 2^-e (exact in fp64; the fp32 value it is
+ * rounded from is exact too, except below the fp32 normal range, where the
+ * e4m3 result is a signed zero either way). */
+static uint8_t e8m0_code(float v, int e)
+{
+    return orc_e4m3_from_float((float)ldexp((double)v, -e));
+}
+
+static int64_t e8m0_pitch(int64_t KB)
+{
+    return (KB + 3) / 4 * 4;
+}
+
+/* Per-token quantization with power-of-two scales: q[M][K] e4m3 codes,
+ * s[M][KBp] exponent bytes, KBp = K/128 rounded up to a multiple of 4. */
+void orc_quantize_per_token_e8m0(const float* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s)
+{
+    int64_t KB = K / 128, KBp = e8m0_pitch(KB);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const float* blk = x + m * K + kb * 128;
+            float amax = 0.0f;
+            for (int k = 0; k < 128; ++k) {
+                float a = fabsf(blk[k]);
+                if (a > amax)
+                    amax = a;
+            }
+            int e = orc_e8m0_exponent(amax);
+            s[m * KBp + kb] = (uint8_t)(e + 127);
+            for (int k = 0; k < 128; ++k)
+                q[m * K + kb * 128 + k] = e8m0_code(blk[k], e);
+        }
+    }
+}
+
+/* Per-block (128x128) quantization with power-of-two scales: q[N][K],
+ * s[ceil(N/128)][KBp]. */
+void orc_quantize_per_block_e8m0(const float* x, int64_t N, int64_t K, uint8_t* q, uint8_t* s)
+{
+    int64_t KB = K / 128, KBp = e8m0_pitch(KB), NB = (N + 127) / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t nb = 0; nb < NB; ++nb) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            int64_t n_end = (nb + 1) * 128 < N ? (nb + 1) * 128 : N;
+            float amax = 0.0f;
+            for (int64_t n = nb * 128; n < n_end; ++n)
+                for (int k = 0; k < 128; ++k) {
+                    float a = fabsf(x[n * K + kb * 128 + k]);
+                    if (a > amax)
+                        amax = a;
+                }
+            int e = orc_e8m0_exponent(amax);
+            s[nb * KBp + kb] = (uint8_t)(e + 127);
+            for (int64_t n = nb * 128; n < n_end; ++n)
+                for (int k = 0; k < 128; ++k)
+                    q[n * K + kb * 128 + k] = e8m0_code(x[n * K + kb * 128 + k], e);
+        }
+    }
+}
+
 /* ----------------------------------------------------------------- GEMM */
 
 /* One output row of the block-scaled NT GEMM, straight from the definition:
