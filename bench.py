@@ -75,7 +75,7 @@ def algorithmic(case):
     groups = case.active_groups
     byts = (rows * case.K                     # A codes
             + groups * case.N * case.K        # B codes of groups in use
-            + 4 * (rows * KB + groups * NB * KB)   # scales
+            + (1 if case.scales == "e8m0" else 4) * (rows * KB + groups * NB * KB)   # scales
             + 2 * rows * case.N)              # bf16 D
     if case.x_c is not None:
         byts += 4 * rows * case.N             # fp32 C
@@ -109,13 +109,16 @@ def make_inputs(case, dev, dg):
     x_a = case.x_a.to(dev)
     x_b = case.x_b.to(dev)
     K = case.K
-    qa, sa = dg.dg_quantize_fp8_per_token(x_a.reshape(-1, K))
+    e8 = case.scales == "e8m0"
+    q_token = dg.dg_quantize_fp8_per_token_e8m0 if e8 else dg.dg_quantize_fp8_per_token
+    q_block = dg.dg_quantize_fp8_per_block_e8m0 if e8 else dg.dg_quantize_fp8_per_block
+    qa, sa = q_token(x_a.reshape(-1, K))
     qa = qa.reshape(x_a.shape)
-    sa = sa.reshape(*x_a.shape[:-1], K // 128)
+    sa = sa.reshape(*x_a.shape[:-1], sa.shape[-1])
     if x_b.dim() == 2:
-        qb, sb = dg.dg_quantize_fp8_per_block(x_b)
+        qb, sb = q_block(x_b)
     else:
-        parts = [dg.dg_quantize_fp8_per_block(x_b[g].contiguous()) for g in range(x_b.shape[0])]
+        parts = [q_block(x_b[g].contiguous()) for g in range(x_b.shape[0])]
         qb = torch.stack([p[0] for p in parts])
         sb = torch.stack([p[1] for p in parts])
     aux = None
@@ -133,6 +136,14 @@ def make_inputs(case, dev, dg):
 
 
 def gemm_call(case, dg, t):
+    if case.scales == "e8m0":
+        if case.form == "dense":
+            dg.dg_fp8_gemm_nt_e8m0(t["A"], t["sa"], t["B"], t["sb"], t["D"])
+        elif case.form == "contiguous":
+            dg.dg_fp8_gemm_grouped_contiguous_e8m0(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
+        else:
+            dg.dg_fp8_gemm_grouped_masked_e8m0(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
+        return
     if case.form == "dense":
         dg.dg_fp8_gemm_nt(t["A"], t["sa"], t["B"], t["sb"], t["D"])
     elif case.form == "dense_acc":
@@ -153,40 +164,45 @@ def time_quantize(dg, t, case, reps=20):
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.empty((x.shape[0], case.K // 128), dtype=torch.float32, device=x.device)
 
-    def timed(fn, src):
+    def timed(fn, src, q_, s_):
         for _ in range(3):
-            fn(src, q, s)
+            fn(src, q_, s_)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            fn(src, q, s)
+            fn(src, q_, s_)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms = timed(dg.dg_quantize_fp8_per_token, x)
-    ms_b = timed(dg.dg_quantize_fp8_per_token_bf16, xb)
+    KB, SP = case.K // 128, dg.e8m0_pitch(case.K // 128)
+    s8 = torch.zeros((x.shape[0], SP), dtype=torch.uint8, device=x.device)
+    ms = timed(dg.dg_quantize_fp8_per_token, x, q, s)
+    ms_b = timed(dg.dg_quantize_fp8_per_token_bf16, xb, q, s)
+    ms_e = timed(dg.dg_quantize_fp8_per_token_e8m0, x, q, s8)
     w = t["x_b"].reshape(-1, case.K) if t["x_b"].dim() == 2 else t["x_b"][0]
+    NB = (w.shape[0] + 127) // 128
     qw = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    sw = torch.empty(((w.shape[0] + 127) // 128, case.K // 128), dtype=torch.float32,
-                     device=w.device)
-    for _ in range(3):
-        dg.dg_quantize_fp8_per_block(w, qw, sw)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dg.dg_quantize_fp8_per_block(w, qw, sw)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_w = e0.elapsed_time(e1) / reps
+    sw = torch.empty((NB, KB), dtype=torch.float32, device=w.device)
+    sw8 = torch.zeros((NB, SP), dtype=torch.uint8, device=w.device)
+    ms_w = timed(dg.dg_quantize_fp8_per_block, w, qw, sw)
+    ms_we = timed(dg.dg_quantize_fp8_per_block_e8m0, w, qw, sw8)
     byts = x.numel() * 5 + s.numel() * 4
     byts_b = x.numel() * 3 + s.numel() * 4
+    byts_e = x.numel() * 5 + x.shape[0] * KB
+    byts_w = w.numel() * 5 + NB * KB * 4
+    byts_we = w.numel() * 5 + NB * KB
+
+    def gbs(b, m):
+        return round(b / (m * 1e-3) / 1e9, 1)
+
     return {"kernel": "quantize_per_token", "rows": int(x.shape[0]), "K": case.K,
-            "us": round(ms * 1e3, 2), "GB/s": round(byts / (ms * 1e-3) / 1e9, 1),
-            "bf16_input_us": round(ms_b * 1e3, 2),
-            "bf16_input_GB/s": round(byts_b / (ms_b * 1e-3) / 1e9, 1),
+            "us": round(ms * 1e3, 2), "GB/s": gbs(byts, ms),
+            "bf16_input_us": round(ms_b * 1e3, 2), "bf16_input_GB/s": gbs(byts_b, ms_b),
+            "e8m0_us": round(ms_e * 1e3, 2), "e8m0_GB/s": gbs(byts_e, ms_e),
             "per_block_rows": int(w.shape[0]), "per_block_us": round(ms_w * 1e3, 2),
-            "per_block_GB/s": round((w.numel() * 5 + sw.numel() * 4) / (ms_w * 1e-3) / 1e9, 1)}
+            "per_block_GB/s": gbs(byts_w, ms_w),
+            "per_block_e8m0_us": round(ms_we * 1e3, 2), "per_block_e8m0_GB/s": gbs(byts_we, ms_we)}
 
 
 def cpu_baseline(case, target_s: float):
@@ -196,36 +212,40 @@ def cpu_baseline(case, target_s: float):
     import oracle
 
     K = case.K
+    e8 = case.scales == "e8m0"
+    q_token = oracle.quantize_per_token_e8m0 if e8 else oracle.quantize_per_token
+    q_block = oracle.quantize_per_block_e8m0 if e8 else oracle.quantize_per_block
+    dense = oracle.gemm_nt_e8m0 if e8 else oracle.gemm_nt
+    contiguous = oracle.gemm_grouped_contiguous_e8m0 if e8 else oracle.gemm_grouped_contiguous
+    masked = oracle.gemm_grouped_masked_e8m0 if e8 else oracle.gemm_grouped_masked
     xa = case.x_a.reshape(-1, K).numpy()
     if case.form in ("dense", "dense_acc"):
-        qb, sb = oracle.quantize_per_block(case.x_b.numpy())
+        qb, sb = q_block(case.x_b.numpy())
         routed = np.arange(case.M)
     elif case.form == "contiguous":
-        parts = [oracle.quantize_per_block(np.ascontiguousarray(case.x_b[g].numpy()))
-                 for g in range(case.G)]
+        parts = [q_block(np.ascontiguousarray(case.x_b[g].numpy())) for g in range(case.G)]
         qb = np.stack([p[0] for p in parts]); sb = np.stack([p[1] for p in parts])
         lay = case.layout.numpy()
         routed = np.nonzero((lay >= 0) & (lay < case.G))[0]
     else:
-        parts = [oracle.quantize_per_block(np.ascontiguousarray(case.x_b[g].numpy()))
-                 for g in range(case.G)]
+        parts = [q_block(np.ascontiguousarray(case.x_b[g].numpy())) for g in range(case.G)]
         qb = np.stack([p[0] for p in parts]); sb = np.stack([p[1] for p in parts])
         mm = np.clip(case.masked_m.numpy(), 0, case.M)
         routed = np.concatenate([g * case.M + np.arange(mm[g]) for g in range(case.G)])
-    qa, sa = oracle.quantize_per_token(xa)
+    qa, sa = q_token(xa)
 
     def run(rows):
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         t0 = time.perf_counter()
         if case.form == "dense":
-            oracle.gemm_nt(qa, sa, qb, sb, rows=rows)
+            dense(qa, sa, qb, sb, rows=rows)
         elif case.form == "dense_acc":
             oracle.gemm_nt_acc(qa[rows], sa[rows], qb, sb, case.x_c.numpy()[rows])
         elif case.form == "contiguous":
-            oracle.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=rows)
+            contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=rows)
         else:
-            oracle.gemm_grouped_masked(qa.reshape(case.G, case.M, K), sa.reshape(case.G, case.M, -1),
-                                       qb, sb, case.masked_m.numpy(), rows=rows)
+            masked(qa.reshape(case.G, case.M, K), sa.reshape(case.G, case.M, -1),
+                   qb, sb, case.masked_m.numpy(), rows=rows)
         return time.perf_counter() - t0
 
     threads = oracle.num_threads()
@@ -301,7 +321,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = traffic_from_profiles(case.name)
-    roof["kernel"] = f"gemm_kernel ({case.form})"
+    roof["kernel"] = f"gemm_kernel ({case.form}, {case.scales} scales)"
     roof["kernel_us"] = round(kernel_ms * 1e3, 2)
     roof["algorithmic_flop"] = flop
     roof["algorithmic_bytes"] = byts
@@ -314,7 +334,8 @@ def main():
         "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": case.name, "form": case.form, "M": case.M, "N": case.N,
+        "config": {"workload": case.name, "form": case.form, "scales": case.scales,
+                   "M": case.M, "N": case.N,
                    "K": case.K, "G": case.G, "valid_rows": case.valid_rows,
                    "rotated_input_sets": copies},
         "roofline": roof,

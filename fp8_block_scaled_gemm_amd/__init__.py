@@ -26,6 +26,8 @@ __all__ = [
     "dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_fp8_gemm_grouped_contiguous",
     "dg_fp8_gemm_grouped_masked",
     "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16", "dg_quantize_fp8_per_block",
+    "dg_fp8_gemm_nt_e8m0", "dg_fp8_gemm_grouped_contiguous_e8m0", "dg_fp8_gemm_grouped_masked_e8m0",
+    "dg_quantize_fp8_per_token_e8m0", "dg_quantize_fp8_per_block_e8m0", "e8m0_pitch",
     "dg_status_string",
 ]
 
@@ -64,6 +66,11 @@ def load_library():
         ("dg_quantize_fp8_per_token", [p, i64, i64, p, p, p]),
         ("dg_quantize_fp8_per_token_bf16", [p, i64, i64, p, p, p]),
         ("dg_quantize_fp8_per_block", [p, i64, i64, p, p, p]),
+        ("dg_fp8_gemm_nt_e8m0", [p, p, p, p, p, i64, i64, i64, p]),
+        ("dg_fp8_gemm_grouped_contiguous_e8m0", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
+        ("dg_fp8_gemm_grouped_masked_e8m0", [p, p, p, p, p, p, i64, i64, i64, i64, p]),
+        ("dg_quantize_fp8_per_token_e8m0", [p, i64, i64, p, p, p]),
+        ("dg_quantize_fp8_per_block_e8m0", [p, i64, i64, p, p, p]),
     ]:
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -215,5 +222,89 @@ def dg_quantize_fp8_per_block(x, q=None, s=None):
     q = _bytes(q, "q")
     _check(q, "q", shape=(N, K)); _check(s, "s", torch.float32, (NB, K // 128))
     _call("dg_quantize_fp8_per_block", x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
+          _stream_ptr(x))
+    return q, s
+
+
+# ------------------------------------------------ power-of-two (E8M0) scales
+
+def e8m0_pitch(kb: int) -> int:
+    """Bytes per row of E8M0 scales: K/128 rounded up to a multiple of 4."""
+    return (kb + 3) // 4 * 4
+
+
+def dg_fp8_gemm_nt_e8m0(A, sa, B, sb, D):
+    """Dense form with E8M0 scales sa[M][SP], sb[ceil(N/128)][SP] (uint8)."""
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    SP, NB = e8m0_pitch(K // 128), (N + 127) // 128
+    _check(A, "A"); _check(B, "B", shape=(N, K))
+    _check(sa, "sa", torch.uint8, (M, SP)); _check(sb, "sb", torch.uint8, (NB, SP))
+    _check(D, "D", _D_TYPES, (M, N))
+    _call("dg_fp8_gemm_nt_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+          D.data_ptr(), M, N, K, _stream_ptr(D))
+    return D
+
+
+def dg_fp8_gemm_grouped_contiguous_e8m0(A, sa, B, sb, D, grouped_layout):
+    """Contiguous-grouped form with E8M0 scales sa[M_sum][SP], sb[G][NB][SP]."""
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    M_sum, K = A.shape
+    G, N, _ = B.shape
+    SP, NB = e8m0_pitch(K // 128), (N + 127) // 128
+    _check(A, "A"); _check(B, "B", shape=(G, N, K))
+    _check(sa, "sa", torch.uint8, (M_sum, SP)); _check(sb, "sb", torch.uint8, (G, NB, SP))
+    _check(D, "D", _D_TYPES, (M_sum, N))
+    _check(grouped_layout, "grouped_layout", torch.int32, (M_sum,))
+    _call("dg_fp8_gemm_grouped_contiguous_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+          sb.data_ptr(), D.data_ptr(), grouped_layout.data_ptr(), M_sum, N, K, G, _stream_ptr(D))
+    return D
+
+
+def dg_fp8_gemm_grouped_masked_e8m0(A, sa, B, sb, D, masked_m):
+    """Masked-grouped form with E8M0 scales sa[G][M_max][SP], sb[G][NB][SP]."""
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    G, M_max, K = A.shape
+    _, N, _ = B.shape
+    SP, NB = e8m0_pitch(K // 128), (N + 127) // 128
+    _check(A, "A"); _check(B, "B", shape=(G, N, K))
+    _check(sa, "sa", torch.uint8, (G, M_max, SP)); _check(sb, "sb", torch.uint8, (G, NB, SP))
+    _check(D, "D", _D_TYPES, (G, M_max, N))
+    _check(masked_m, "masked_m", torch.int32, (G,))
+    _call("dg_fp8_gemm_grouped_masked_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+          sb.data_ptr(), D.data_ptr(), masked_m.data_ptr(), G, M_max, N, K, _stream_ptr(D))
+    return D
+
+
+def dg_quantize_fp8_per_token_e8m0(x, q=None, s=None):
+    """x[M][K] fp32 -> (q[M][K] uint8 codes, s[M][SP] uint8 E8M0 exponents).
+    A newly allocated s has zero padding bytes; the kernel never writes them."""
+    _check(x, "x", torch.float32)
+    M, K = x.shape
+    SP = e8m0_pitch(K // 128)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.zeros((M, SP), dtype=torch.uint8, device=x.device)
+    q = _bytes(q, "q")
+    _check(q, "q", shape=(M, K)); _check(s, "s", torch.uint8, (M, SP))
+    _call("dg_quantize_fp8_per_token_e8m0", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
+          _stream_ptr(x))
+    return q, s
+
+
+def dg_quantize_fp8_per_block_e8m0(x, q=None, s=None):
+    """x[N][K] fp32 -> (q[N][K] uint8, s[ceil(N/128)][SP] uint8 E8M0 exponents)."""
+    _check(x, "x", torch.float32)
+    N, K = x.shape
+    NB, SP = (N + 127) // 128, e8m0_pitch(K // 128)
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.zeros((NB, SP), dtype=torch.uint8, device=x.device)
+    q = _bytes(q, "q")
+    _check(q, "q", shape=(N, K)); _check(s, "s", torch.uint8, (NB, SP))
+    _call("dg_quantize_fp8_per_block_e8m0", x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s

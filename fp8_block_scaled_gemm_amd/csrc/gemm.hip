@@ -35,6 +35,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 namespace dg {
 
@@ -140,6 +141,16 @@ __device__ __forceinline__ v4f mfma_block(const v8i& b, const v8i& a) {
     // format 0 = e4m3 for both operands; zero scale operands select the
     // unscaled instruction
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// acc + 2^(eb-127) * 2^(ea-127) * (B_blk A_blk^T) in one instruction.  Each
+// lane passes one E8M0 byte per operand in bits 0-7 (opsel 0): operand 0's
+// (eb) applies to B row (lane & 15) of the sub-tile, operand 1's (ea) to A
+// row (lane & 15), each for the 32-wide K group (lane >> 4); a block's four
+// groups share one scale, so every lane passes its row's block scale.
+__device__ __forceinline__ v4f mfma_block_e8(const v8i& b, const v8i& a, const v4f& c, int eb,
+                                              int ea) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea);
 }
 
 __device__ __forceinline__ v8i join(const v4u& lo, const v4u& hi) {
@@ -282,12 +293,20 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
 //     barrier) into a second register set.
 // So no barrier is followed by a burst of B fragment reads that would leave
 // the matrix cores idle; only the first A fragment of a step waits for LDS.
-template <class T, Form kForm>
+//
+// Scales (kE8 = false): fp32, [rows][K/128] and [groups][NB][K/128], each K
+// block's partial promoted as acc += (sa sb) P.  With kE8: E8M0 exponent
+// bytes, rows padded to a multiple of 4 bytes ([rows][SP], [groups][NB][SP]),
+// applied by the scaled MFMA itself, which accumulates straight into acc.
+template <class T, Form kForm, bool kE8>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
-    const float* __restrict__ sb, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
+    const uint8_t* __restrict__ A, const void* __restrict__ sa_v, const uint8_t* __restrict__ B,
+    const void* __restrict__ sb_v, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
     const float* __restrict__ C, int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks,
     int n_blocks) {
+    using ScaleT = typename std::conditional<kE8, uint8_t, float>::type;
+    const ScaleT* __restrict__ sa = static_cast<const ScaleT*>(sa_v);
+    const ScaleT* __restrict__ sb = static_cast<const ScaleT*>(sb_v);
     // Two A stages then two B stages (after the K loop: the bf16 output tile).
     // Scales come in chunks of four K blocks, two chunk buffers: row scales
     // as [row][4], column-block scales as [block][4].
@@ -300,6 +319,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     const int lane = tid & 63;
     const int KB = (int)(K >> 7);
     const int NB = (int)((N + 127) >> 7);
+    const int SP = kE8 ? ((KB + 3) & ~3) : KB;  // scales per scale row
     const int lr = lane & 15, lg = lane >> 4;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
     const int wcol = wn * T::WN;
@@ -319,11 +339,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // count towards the wave's vmcnt like every other step's.
     const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
     const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
-    // scale chunk loads: wave w < BM/64 fetches 16 bytes (four K blocks) of
-    // the row scales of rows [64w, 64w + 64), the next wave the column-block
-    // scales (lane l: block l / 4, K block l % 4 of the chunk)
-    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)KB * 4;
-    const uint32_t offSB = ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
+    // scale chunk loads: wave w < BM/64 fetches the four K blocks' row
+    // scales of rows [64w, 64w + 64) (16 bytes per row, or one 4-byte word
+    // of exponents), the next wave the column-block scales (fp32: lane l
+    // gets block l / 4, K block l % 4 of the chunk; E8M0: lane l gets the
+    // word of block l)
+    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)SP * (kE8 ? 1 : 4);
+    const uint32_t offSB = kE8 ? (uint32_t)lane * (uint32_t)SP
+                               : ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
     constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
     static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
     const int nb0 = ti.n0 >> 7;
@@ -331,9 +354,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // column-scale blocks the tile touches
     const int vnb = (int)((ti.n0 + vn - 1) >> 7) - nb0 + 1;
     const uint8_t* tileA = A + ti.arow0 * K;
-    const float* tileSA = sa + ti.arow0 * KB;
+    const ScaleT* tileSA = sa + ti.arow0 * SP;
     const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
-    const float* tileSB = sb + ((int64_t)ti.g * NB + nb0) * KB;
+    const ScaleT* tileSB = sb + ((int64_t)ti.g * NB + nb0) * SP;
 #define DG_ISSUE_A_PART(kb_, st_, i0_, i1_)                                                       \
     do {                                                                                          \
         const v4u rs_ = buffer_rsrc(tileA + (kb_) * 128,                                          \
@@ -359,17 +382,22 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1.  The
     // range check of a buffer load is per 4-byte word, so the words of a row's
     // last chunk past K/128 (and rows past the valid ones) read as zero or as
-    // the next row's scales, which no step uses.
+    // the next row's scales, which no step uses.  An exponent row's padding
+    // to 4 bytes keeps its chunk words aligned and in range.
 #define DG_ISSUE_SCALES(c_)                                                                       \
     do {                                                                                          \
         const int kb0_ = (c_) * 4;                                                                \
+        constexpr uint32_t kSz_ = sizeof(ScaleT);                                                 \
         if (kb0_ < KB) {                                                                          \
             if (wave < kScaleWaves) {                                                             \
-                load_lds_16(buffer_rsrc(tileSA + kb0_, (uint32_t)(ti.valid * KB - kb0_) * 4),    \
-                            offSA, &smSA[(c_) & 1][wave * 64 * 4]);                               \
+                const v4u rs_ = buffer_rsrc(tileSA + kb0_, (uint32_t)(ti.valid * SP - kb0_) * kSz_); \
+                if (kE8)                                                                          \
+                    load_lds_4(rs_, offSA, &smSA[(c_) & 1][wave * 64]);                           \
+                else                                                                              \
+                    load_lds_16(rs_, offSA, &smSA[(c_) & 1][wave * 64 * 4]);                      \
             } else if (wave == kScaleWaves) {                                                     \
-                load_lds_4(buffer_rsrc(tileSB + kb0_, (uint32_t)(vnb * KB - kb0_) * 4),          \
-                           lane < 4 * vnb ? offSB : 0xffffff00u, &smSB[(c_) & 1][0]);             \
+                load_lds_4(buffer_rsrc(tileSB + kb0_, (uint32_t)(vnb * SP - kb0_) * kSz_),       \
+                           lane < (kE8 ? 1 : 4) * vnb ? offSB : 0xffffff00u, &smSB[(c_) & 1][0]); \
             }                                                                                     \
         }                                                                                         \
     } while (0)
@@ -408,6 +436,24 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_
 #define DG_ROWS(bf_use, kb_, st_, i0_, i1_)                                                       \
     do {                                                                                          \
+        if constexpr (kE8) {                                                                      \
+            /* exponent chunks: one 4-byte word per row / column block */                        \
+            const uint8_t* eSA_ =                                                                 \
+                reinterpret_cast<const uint8_t*>(smSA[((kb_) >> 2) & 1]) + ((kb_) & 3);            \
+            const uint8_t* eSB_ =                                                                 \
+                reinterpret_cast<const uint8_t*>(smSB[((kb_) >> 2) & 1]) + ((kb_) & 3);            \
+            int e_b_[T::kOneScaleB ? 1 : T::TN];                                                  \
+            _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)               \
+                e_b_[j] = eSB_[sblk[j] * 4];                                                      \
+            _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                               \
+                const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);   \
+                const int e_a_ = eSA_[(srow + kRowStep * i) * 4];                                 \
+                _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                 \
+                    acc[i][j] = mfma_block_e8(bf_use[j], af_, acc[i][j],                          \
+                                              e_b_[T::kOneScaleB ? 0 : j], e_a_);                 \
+            }                                                                                     \
+            break;                                                                                \
+        }                                                                                         \
         const float* sSA_ = &smSA[((kb_) >> 2) & 1][(kb_) & 3];                                   \
         const float* sSB_ = &smSB[((kb_) >> 2) & 1][(kb_) & 3];                                   \
         float s_b_[T::kOneScaleB ? 1 : T::TN];                                                    \
@@ -565,7 +611,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     }
 }
 
-template <class T, Form kForm>
+template <class T, Form kForm, bool kE8>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t m_blocks = (a.rows + T::BM - 1) / T::BM;
     const int64_t n_blocks = (a.N + T::BN - 1) / T::BN;
@@ -583,7 +629,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     // and a tile's rows of fp32 C
     if (kForm == Form::DenseAcc && (int64_t)T::BM * a.N * 4 >= (int64_t(1) << 32))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<T, kForm>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<T, kForm, kE8>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
                        a.A, a.sa, a.B, a.sb, a.D, a.aux, a.C, a.rows, a.N, a.K, a.G, (int)m_blocks,
                        (int)n_blocks);
     return hipGetLastError();
@@ -631,20 +677,16 @@ static int forced_dense_shape() {
 // ceil(tiles / CUs) rounds of one tile's time.  A tile's time scales with its
 // area times a per-shape cost per output element (narrower tiles re-read
 // more fragments per MFMA); pick the shape with the least estimated time.
-template <Form kForm>
+template <Form kForm, bool kE8>
 static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     struct Shape { int bm, bn; double rel; };
     static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.05}, {256, 192, 1.10},
                                     {128, 256, 1.15}};
-    // the accumulating epilogue stages fp32 rows of a power-of-two width
-    const bool acc = kForm == Form::DenseAcc;
     const int64_t cus = device_cus();
     int best = forced_dense_shape();
-    if (acc && (best == 1 || best == 2)) best = -1;
     if (best < 0) {
         double best_cost = 0;
         for (int i = 0; i < 4; ++i) {
-            if (acc && (i == 1 || i == 2)) continue;
             const Shape& sh = kShapes[i];
             const int64_t tiles = ((a.rows + sh.bm - 1) / sh.bm) * ((a.N + sh.bn - 1) / sh.bn);
             const double cost = (double)((tiles + cus - 1) / cus) * sh.bm * sh.bn * sh.rel;
@@ -654,25 +696,28 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
             }
         }
     }
-    if constexpr (kForm == Form::DenseAcc) {
-        if (best == 3) return launch_tiled<TileRows128, kForm>(a, stream);
-        return launch_tiled<TileLarge, kForm>(a, stream);
-    } else {
-        switch (best) {
-            case 1: return launch_tiled<TileWide224, kForm>(a, stream);
-            case 2: return launch_tiled<TileWide192, kForm>(a, stream);
-            case 3: return launch_tiled<TileRows128, kForm>(a, stream);
-            default: return launch_tiled<TileLarge, kForm>(a, stream);
-        }
+    switch (best) {
+        case 1: return launch_tiled<TileWide224, kForm, kE8>(a, stream);
+        case 2: return launch_tiled<TileWide192, kForm, kE8>(a, stream);
+        case 3: return launch_tiled<TileRows128, kForm, kE8>(a, stream);
+        default: return launch_tiled<TileLarge, kForm, kE8>(a, stream);
     }
 }
 
 hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
+    if (a.e8m0) {
+        switch (form) {
+            case Form::Dense: return launch_dense<Form::Dense, true>(a, stream);
+            case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous, true>(a, stream);
+            case Form::Masked: return launch_tiled<TileMasked, Form::Masked, true>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (form) {
-        case Form::Dense: return launch_dense<Form::Dense>(a, stream);
-        case Form::DenseAcc: return launch_dense<Form::DenseAcc>(a, stream);
-        case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous>(a, stream);
-        case Form::Masked: return launch_tiled<TileMasked, Form::Masked>(a, stream);
+        case Form::Dense: return launch_dense<Form::Dense, false>(a, stream);
+        case Form::DenseAcc: return launch_dense<Form::DenseAcc, false>(a, stream);
+        case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous, false>(a, stream);
+        case Form::Masked: return launch_tiled<TileMasked, Form::Masked, false>(a, stream);
     }
     return hipErrorInvalidValue;
 }

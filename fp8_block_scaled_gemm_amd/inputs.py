@@ -8,7 +8,8 @@ Recipe (one CPU ``torch.Generator`` per case, seeded with the case's seed):
 group sizes or masks are drawn first (``torch.randint``), then the fp32
 activation matrix ``x_a`` (``torch.randn``), then the fp32 weight matrix
 ``x_b`` (``torch.randn``).  The fp32 matrices are quantized afterwards by the
-caller: per token (1x128) for A and per 128x128 block for B.
+caller: per token (1x128) for A and per 128x128 block for B, with fp32
+scales or, for the cases marked ``scales="e8m0"``, power-of-two scales.
 
 The workloads follow DeepSeek-style projection and MoE expert shapes; no
 dataset is involved.
@@ -32,6 +33,7 @@ class Case:
     layout: int32 [M_sum] group id per row, -1 on padding (contiguous).
     masked_m: int32 [G] valid rows per group (masked).
     x_c:  fp32 addend [M][N] (dense_acc).
+    scales: "fp32" (amax/448) or "e8m0" (power-of-two exponent bytes).
     """
     name: str
     form: str
@@ -45,6 +47,7 @@ class Case:
     masked_m: torch.Tensor | None = None
     group_rows: list = field(default_factory=list)
     x_c: torch.Tensor | None = None
+    scales: str = "fp32"
 
     @property
     def valid_rows(self) -> int:
@@ -136,6 +139,23 @@ WORKLOADS = {
     "masked_16x256x4096x7168": lambda: masked_case(16, 256, 4096, 7168, 5, name="masked_16x256x4096x7168"),
     "masked_16x256x7168x2048": lambda: masked_case(16, 256, 7168, 2048, 51, name="masked_16x256x7168x2048"),
 }
+
+
+def _e8m0(case: Case) -> Case:
+    case.scales = "e8m0"
+    return case
+
+
+WORKLOADS.update({
+    "dense_e8m0_4096x7168x2048": lambda: _e8m0(dense_case(4096, 7168, 2048, 2,
+                                                          "dense_e8m0_4096x7168x2048")),
+    "dense_e8m0_4096x24576x1536": lambda: _e8m0(dense_case(4096, 24576, 1536, 3,
+                                                           "dense_e8m0_4096x24576x1536")),
+    "contiguous_e8m0_8x4096x7168": lambda: _e8m0(contiguous_case(
+        8, 4096, 7168, 4, name="contiguous_e8m0_8x4096x7168")),
+    "masked_e8m0_16x256x4096x7168": lambda: _e8m0(masked_case(
+        16, 256, 4096, 7168, 5, name="masked_e8m0_16x256x4096x7168")),
+})
 
 
 def workload(name: str) -> Case:

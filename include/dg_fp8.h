@@ -136,6 +136,47 @@ dg_status dg_quantize_fp8_per_token_bf16(const uint16_t* x, int64_t M, int64_t K
 dg_status dg_quantize_fp8_per_block(const float* x, int64_t N, int64_t K,
                                     uint8_t* q, float* s, void* stream);
 
+/* ---- Power-of-two (E8M0) scales.
+ * The same three forms with each block scale a power of two, held as one
+ * E8M0 exponent byte (2^(b-127); 255 is NaN), for the hardware block-scaled
+ * matrix instruction: the Gluon tutorial page "TCGen05 Copy Instruction",
+ * section on tensor scales, hands per-block scales to the scaled MMA, which
+ * applies them itself (here: v_mfma_scale_f32_16x16x128_f8f6f4, so no
+ * per-block promotion step).  Blocks are the same 1x128 (A) and 128x128 (B)
+ * blocks; the result is the dense form's definition with sa, sb replaced by
+ * their powers of two.
+ * Scale rows hold K/128 bytes padded to SP = K/128 rounded up to a multiple
+ * of 4 (padding bytes are neither read nor written):
+ *   dense:      sa [M][SP]            sb [ceil(N/128)][SP]
+ *   contiguous: sa [M_sum][SP]        sb [G][ceil(N/128)][SP]
+ *   masked:     sa [G][M_max][SP]     sb [G][ceil(N/128)][SP]
+ * Everything else (operands, routing, sizes, errors) is as for the fp32-scale
+ * entry point of the same form. */
+dg_status dg_fp8_gemm_nt_e8m0(const uint8_t* A, const uint8_t* sa,
+                              const uint8_t* B, const uint8_t* sb,
+                              uint16_t* D, int64_t M, int64_t N, int64_t K, void* stream);
+dg_status dg_fp8_gemm_grouped_contiguous_e8m0(const uint8_t* A, const uint8_t* sa,
+                                              const uint8_t* B, const uint8_t* sb,
+                                              uint16_t* D, const int32_t* grouped_layout,
+                                              int64_t M_sum, int64_t N, int64_t K, int64_t G,
+                                              void* stream);
+dg_status dg_fp8_gemm_grouped_masked_e8m0(const uint8_t* A, const uint8_t* sa,
+                                          const uint8_t* B, const uint8_t* sb,
+                                          uint16_t* D, const int32_t* masked_m,
+                                          int64_t G, int64_t M_max, int64_t N, int64_t K,
+                                          void* stream);
+
+/* Quantization with power-of-two scales (the recipe is not on the pages):
+ * a block's exponent is the smallest e >= -127 with amax <= 448 * 2^e, its
+ * byte e + 127, and q = e4m3 of x * 2^-e (an exact scaling; round to nearest
+ * even, never past 448).  Per token: x [M][K] fp32 -> q [M][K],
+ * s [M][SP].  Per block: x [N][K] fp32 -> q [N][K], s [ceil(N/128)][SP].
+ * Sizes and errors as for the fp32-scale quantizers. */
+dg_status dg_quantize_fp8_per_token_e8m0(const float* x, int64_t M, int64_t K,
+                                         uint8_t* q, uint8_t* s, void* stream);
+dg_status dg_quantize_fp8_per_block_e8m0(const float* x, int64_t N, int64_t K,
+                                         uint8_t* q, uint8_t* s, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* dg_status_string(dg_status status);
 

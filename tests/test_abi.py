@@ -34,7 +34,10 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_fp8_gemm_grouped_contiguous",
         "dg_fp8_gemm_grouped_masked", "dg_quantize_fp8_per_token", "dg_quantize_fp8_per_token_bf16",
-        "dg_quantize_fp8_per_block", "dg_status_string"])
+        "dg_quantize_fp8_per_block", "dg_status_string",
+        "dg_fp8_gemm_nt_e8m0", "dg_fp8_gemm_grouped_contiguous_e8m0",
+        "dg_fp8_gemm_grouped_masked_e8m0", "dg_quantize_fp8_per_token_e8m0",
+        "dg_quantize_fp8_per_block_e8m0"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -102,6 +105,27 @@ def test_acc_rejections(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 128, None) == DG_ERR_SHAPE  # N % 8
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 100, None) == DG_ERR_SHAPE   # K % 128
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1 << 22, 128, None) == DG_ERR_SHAPE  # N
+
+
+def test_e8m0_rejections(lib):
+    """The exponent-scale entry points apply the same host checks."""
+    f = lib.dg_fp8_gemm_nt_e8m0
+    assert f(None, None, None, None, None, 0, 8, 128, None) == DG_OK                # M = 0
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 128, None) == DG_ERR_NULL
+    assert f(FAKE, FAKE + 4, FAKE, FAKE, FAKE, 4, 8, 128, None) == DG_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 12, 128, None) == DG_ERR_SHAPE       # N % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 200, None) == DG_ERR_SHAPE        # K % 128
+    c = lib.dg_fp8_gemm_grouped_contiguous_e8m0
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 2, None) == DG_ERR_SHAPE
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, None, 128, 8, 128, 2, None) == DG_ERR_NULL
+    m = lib.dg_fp8_gemm_grouped_masked_e8m0
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, 8, 128, None) == DG_ERR_SHAPE
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 8, 128, None) == DG_OK      # no rows
+    for q in (lib.dg_quantize_fp8_per_token_e8m0, lib.dg_quantize_fp8_per_block_e8m0):
+        assert q(FAKE, 4, 100, FAKE, FAKE, None) == DG_ERR_SHAPE
+        assert q(FAKE, 4, 128, FAKE, None, None) == DG_ERR_NULL
+        assert q(FAKE, 0, 128, None, None, None) == DG_OK
+    assert lib.dg_quantize_fp8_per_block_e8m0(FAKE, 128 * 65536, 128, FAKE, FAKE, None) == DG_ERR_SHAPE
 
 
 def test_grouped_rejections(lib):
