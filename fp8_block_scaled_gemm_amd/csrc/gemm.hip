@@ -14,15 +14,17 @@
 //   - The MFMA takes B as its first operand and A as its second, so each lane
 //     owns one output row and four consecutive output columns: one scale
 //     product per lane and sub-tile.
-//   - LDS bandwidth (about 128 bytes per clock per CU for these reads) is the
-//     scarce resource, so only A goes through LDS: its K-slab (128 bytes per
-//     row per K block) is loaded straight from memory into a double-buffered
-//     LDS stage with bounds-checked buffer loads (rows past the valid rows
-//     read as zero and touch no memory).  Each 16-byte chunk of a row sits at
-//     chunk ^ (row & 7), so the 16-lane groups of a fragment read hit distinct
-//     banks.  B fragments are read by each wave straight into registers one K
-//     block ahead; the two waves that share B columns sit on one SIMD and
-//     share them through the L1 cache.
+//   - A and B K-slabs (128 bytes per row per K block) are loaded straight
+//     from memory into double-buffered LDS stages with bounds-checked buffer
+//     loads (rows past the valid rows read as zero and touch no memory), and
+//     fragments are read from there with ds_read_b128.  LDS bandwidth is the
+//     scarce resource (256 bytes per clock without bank conflicts).  The
+//     16-byte chunk c of stage row r sits at c ^ (r & 7), and lane (lr, lg)
+//     of a fragment read takes chunks lg and lg + 4 of row lr: measured
+//     conflict-free, where chunks 2 lg and 2 lg + 1 (any row swizzle tried)
+//     cost two cycles per read.  Which K bytes a lane holds is free as long
+//     as A and B fragments agree; lg, lg + 4 is also the instruction's own
+//     order (K [16 g, 16 g + 16) and [64 + 16 g, +16) for lane group g).
 //   - The output tile is staged through LDS in bf16 and written back in full
 //     16-byte chunks per lane, whole row segments per store instruction
 //     (scattered 8-byte fragment stores reach half the write bandwidth).
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
 
     // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
     // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
-    // belongs at physical chunk l % 8.  A slab's buffer starts at the K block
+    // belongs at physical chunk l % 8 of row 8q + l / 8, i.e. chunk
+    // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  A slab's buffer starts at the K block
     // in row 0 and ends with the tile's last valid row (A) or column (B), so
     // rows past it read as zero; blocks past the last one get an empty
     // buffer, so their loads move no data but still
@@ -405,11 +408,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // ---- fragment reads.  Sub-tile row i of wave row wm covers tile rows
     // [16 (WAVES_M i + wm), +16): the wave rows interleave in 16-row steps, so
     // a partial tile (a masked group's last rows, a ragged M) leaves work on
-    // every wave.  Row r of a stage has (r & 7) == (lr & 7) for every row a
-    // lane reads, so the swizzled chunk offsets are per-lane constants and
+    // every wave.  Every row r a lane reads is lr plus a multiple of 16, so
+    // r & 7 == lr & 7 and the swizzled chunk offsets are per-lane constants;
     // sub-tile i (or j) only adds a multiple of 16 rows (an immediate).
+    static_assert(T::WN % 16 == 0, "wave column offsets keep the row swizzle");
     constexpr int kRowStep = 16 * T::WAVES_M;
-    const int chunk_lo = ((2 * lg) ^ (lr & 7)) << 4, chunk_hi = ((2 * lg + 1) ^ (lr & 7)) << 4;
+    const int chunk_lo = (lg ^ (lr & 7)) << 4, chunk_hi = ((lg + 4) ^ (lr & 7)) << 4;
     const int fragA = (16 * wm + lr) * 128, fragB = (wcol + lr) * 128;
     const int srow = 16 * wm + lr;
     // sub-tile rows of this wave that hold valid rows; the others are skipped
