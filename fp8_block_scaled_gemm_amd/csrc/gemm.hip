@@ -301,7 +301,7 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
 // bytes, rows padded to a multiple of 4 bytes ([rows][SP], [groups][NB][SP]),
 // applied by the scaled MFMA itself, which accumulates straight into acc.
 template <class T, Form kForm, bool kE8>
-__global__ __launch_bounds__(T::kThreads) void gemm_kernel(
+__global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     const uint8_t* __restrict__ A, const void* __restrict__ sa_v, const uint8_t* __restrict__ B,
     const void* __restrict__ sb_v, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
     const float* __restrict__ C, int64_t rows, int64_t N, int64_t K, int64_t G, int m_blocks,
@@ -648,6 +648,9 @@ using TileWide192 = TileConfig<256, 192, 4, 2, 4, false>;
 // 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
 // also the dense shape for few rows.
 using TileRows128 = TileConfig<128, 256, 2, 4, 8, false>;
+// 128x128 tiles, 4 waves of 64x64 (one per SIMD): 64 KiB of stages, so two
+// workgroups share a CU and one's barriers leave the other's MFMAs running.
+using TileSmall = TileConfig<128, 128, 2, 2, 8, false>;
 // Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
 // MFMAs of invalid rows does not shorten them.
 using TileMasked = TileConfig<256, 256, 2, 4, 4, false>;
@@ -665,29 +668,38 @@ static int device_cus() {
     return n;
 }
 
-// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256 pins the dense tile
+// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256|128x128 pins the dense tile
 // shape (for tests and tuning; read at every call); -1 when unset or not
 // one of these.
 static int forced_dense_shape() {
     const char* e = getenv("DG_FP8_DENSE_TILE");
     if (!e) return -1;
-    const char* names[] = {"256x256", "256x224", "256x192", "128x256"};
-    for (int i = 0; i < 4; ++i)
+    const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128"};
+    for (int i = 0; i < 5; ++i)
         if (strcmp(e, names[i]) == 0) return i;
     return -1;
 }
 
-// Dense tile shape: one workgroup per CU at a time, so a launch takes about
-// ceil(tiles / CUs) rounds of one tile's time.  A tile's time scales with its
-// area times a per-shape cost per output element (narrower tiles re-read
-// more fragments per MFMA); pick the shape with the least estimated time.
+// Dense tile shape.  The 256-row shapes and 128x256 run one workgroup per
+// CU, so a launch takes about ceil(tiles / CUs) rounds of one tile's time; a
+// tile's time scales with its area times a per-shape cost per output element
+// (narrower tiles re-read more fragments per MFMA), and the shape with the
+// least estimated time wins.  When even 256x256 tiles would leave half the
+// CUs idle (few rows: decode-sized M), 128x128 tiles are used instead: a
+// lone 128x128 tile takes half the time of a lone 256x256 one (measured
+// 27k against 60k cycles at K = 2048), so the launch finishes sooner; on
+// large problems they are slower (two per CU share it with no gain).
 template <Form kForm, bool kE8>
 static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     struct Shape { int bm, bn; double rel; };
-    static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.05}, {256, 192, 1.10},
-                                    {128, 256, 1.15}};
+    // per-area costs from measured loop cycles per K block (256x256: 3.43k,
+    // 256x224: 3.42k, 256x192: 2.93k, 128x256: 2.08k cycles)
+    static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.15}, {256, 192, 1.15},
+                                    {128, 256, 1.22}};
     const int64_t cus = device_cus();
     int best = forced_dense_shape();
+    const int64_t tiles_large = ((a.rows + 255) / 256) * ((a.N + 255) / 256);
+    if (best < 0 && 2 * tiles_large <= cus) best = 4;
     if (best < 0) {
         double best_cost = 0;
         for (int i = 0; i < 4; ++i) {
@@ -704,6 +716,7 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
         case 1: return launch_tiled<TileWide224, kForm, kE8>(a, stream);
         case 2: return launch_tiled<TileWide192, kForm, kE8>(a, stream);
         case 3: return launch_tiled<TileRows128, kForm, kE8>(a, stream);
+        case 4: return launch_tiled<TileSmall, kForm, kE8>(a, stream);
         default: return launch_tiled<TileLarge, kForm, kE8>(a, stream);
     }
 }
