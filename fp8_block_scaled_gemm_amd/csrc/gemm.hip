@@ -648,9 +648,13 @@ using TileWide192 = TileConfig<256, 192, 4, 2, 4, false>;
 // 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
 // also the dense shape for few rows.
 using TileRows128 = TileConfig<128, 256, 2, 4, 8, false>;
-// 128x128 tiles, 4 waves of 64x64 (one per SIMD): 64 KiB of stages, so two
-// workgroups share a CU and one's barriers leave the other's MFMAs running.
+// Tiles for few rows (decode-sized M), 4 waves each (64x64, 64x32, 64x16):
+// such a launch is bound by how many bytes of B are in flight (each tile
+// keeps about 1.5 K blocks of loads outstanding), so narrower tiles, more of
+// them, stream B faster.
 using TileSmall = TileConfig<128, 128, 2, 2, 8, false>;
+using TileNarrow64 = TileConfig<128, 64, 2, 2, 8, false>;
+using TileNarrow32 = TileConfig<128, 32, 2, 2, 8, false>;
 // Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
 // MFMAs of invalid rows does not shorten them.
 using TileMasked = TileConfig<256, 256, 2, 4, 4, false>;
@@ -668,14 +672,14 @@ static int device_cus() {
     return n;
 }
 
-// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256|128x128 pins the dense tile
+// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256|128x128|128x64|128x32 pins the dense tile
 // shape (for tests and tuning; read at every call); -1 when unset or not
 // one of these.
 static int forced_dense_shape() {
     const char* e = getenv("DG_FP8_DENSE_TILE");
     if (!e) return -1;
-    const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128"};
-    for (int i = 0; i < 5; ++i)
+    const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32"};
+    for (int i = 0; i < 7; ++i)
         if (strcmp(e, names[i]) == 0) return i;
     return -1;
 }
@@ -685,10 +689,10 @@ static int forced_dense_shape() {
 // tile's time scales with its area times a per-shape cost per output element
 // (narrower tiles re-read more fragments per MFMA), and the shape with the
 // least estimated time wins.  When even 256x256 tiles would leave half the
-// CUs idle (few rows: decode-sized M), 128x128 tiles are used instead: a
-// lone 128x128 tile takes half the time of a lone 256x256 one (measured
-// 27k against 60k cycles at K = 2048), so the launch finishes sooner; on
-// large problems they are slower (two per CU share it with no gain).
+// CUs idle (few rows: decode-sized M), 128x32 tiles are used instead: such
+// a launch is latency-bound on B (a lone 256x256 tile takes 60k cycles at
+// K = 2048), and 128x32 tiles put the most B loads in flight (measured on
+// 128 x 7168 x 2048: 13.7 us against 17.7 with 128x128 and 24 with 128x256).
 template <Form kForm, bool kE8>
 static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     struct Shape { int bm, bn; double rel; };
@@ -699,7 +703,7 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     const int64_t cus = device_cus();
     int best = forced_dense_shape();
     const int64_t tiles_large = ((a.rows + 255) / 256) * ((a.N + 255) / 256);
-    if (best < 0 && 2 * tiles_large <= cus) best = 4;
+    if (best < 0 && 2 * tiles_large <= cus) best = 6;
     if (best < 0) {
         double best_cost = 0;
         for (int i = 0; i < 4; ++i) {
@@ -717,6 +721,8 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
         case 2: return launch_tiled<TileWide192, kForm, kE8>(a, stream);
         case 3: return launch_tiled<TileRows128, kForm, kE8>(a, stream);
         case 4: return launch_tiled<TileSmall, kForm, kE8>(a, stream);
+        case 5: return launch_tiled<TileNarrow64, kForm, kE8>(a, stream);
+        case 6: return launch_tiled<TileNarrow32, kForm, kE8>(a, stream);
         default: return launch_tiled<TileLarge, kForm, kE8>(a, stream);
     }
 }
