@@ -284,17 +284,13 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
 // Operands are separate __restrict__ arguments so the compiler knows they
 // are never written during the kernel.
 //
-// Pipeline (one K block = one step, one barrier per step): during step kb
-// each wave
-//   - loads its share of the A slab of block kb+1 (with its row scales and
-//     the tile's column scales) into A stage (kb+1)&1, and of the B slab of
-//     block kb+2 into B stage kb&1, straight from memory into LDS;
-//   - multiplies block kb: B fragments from registers, A fragments streamed
-//     from A stage kb&1 one row of sub-tiles at a time;
-//   - reads its B fragments of block kb+1 (published by the previous
-//     barrier) into a second register set.
-// So no barrier is followed by a burst of B fragment reads that would leave
-// the matrix cores idle; only the first A fragment of a step waits for LDS.
+// Pipeline (one K block = one step, two barriers per step, two stages of A
+// and B in LDS): a step reads its B fragments into registers, multiplies the
+// A rows [0, BM/2) (A fragments streamed from LDS one row of sub-tiles at a
+// time), passes the mid barrier, multiplies the rows [BM/2, BM), and passes
+// the end barrier.  Each wave loads its share of the slabs of block kb+2
+// straight from memory into LDS as soon as a barrier frees their buffer, so
+// every load has one and a half steps to land (see DG_STEP).
 //
 // Scales (kE8 = false): fp32, [rows][K/128] and [groups][NB][K/128], each K
 // block's partial promoted as acc += (sa sb) P.  With kE8: E8M0 exponent
