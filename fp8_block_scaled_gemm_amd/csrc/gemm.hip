@@ -649,6 +649,10 @@ using TileRows128 = TileConfig<128, 256, 2, 4, 8, false>;
 // keeps about 1.5 K blocks of loads outstanding), so narrower tiles, more of
 // them, stream B faster.
 using TileSmall = TileConfig<128, 128, 2, 2, 8, false>;
+// 256x256 tiles, 8 waves of 64x128: each A fragment feeds eight MFMAs.  Used
+// with power-of-two scales (without promotion it fits the registers: 231
+// VGPRs; the fp32-scale kernel spills with it).
+using TileLargeT = TileConfig<256, 256, 4, 2, 4, false>;
 using TileNarrow64 = TileConfig<128, 64, 2, 2, 8, false>;
 using TileNarrow32 = TileConfig<128, 32, 2, 2, 8, false>;
 // Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
@@ -674,8 +678,9 @@ static int device_cus() {
 static int forced_dense_shape() {
     const char* e = getenv("DG_FP8_DENSE_TILE");
     if (!e) return -1;
-    const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32"};
-    for (int i = 0; i < 7; ++i)
+    const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32",
+                           "256x256t"};
+    for (int i = 0; i < 8; ++i)
         if (strcmp(e, names[i]) == 0) return i;
     return -1;
 }
@@ -697,7 +702,8 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.15}, {256, 192, 1.15},
                                     {128, 256, 1.22}};
     const int64_t cus = device_cus();
-    int best = forced_dense_shape();
+    const int forced = forced_dense_shape();
+    int best = forced;
     const int64_t tiles_large = ((a.rows + 255) / 256) * ((a.N + 255) / 256);
     if (best < 0 && 2 * tiles_large <= cus) best = 6;
     if (best < 0) {
@@ -711,6 +717,9 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
                 best = i;
             }
         }
+        // with power-of-two scales the 64x128 wave layout of 256x256 is the
+        // faster one (measured 2-5%)
+        if (kE8 && best == 0) best = 7;
     }
     switch (best) {
         case 1: return launch_tiled<TileWide224, kForm, kE8>(a, stream);
@@ -719,6 +728,7 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
         case 4: return launch_tiled<TileSmall, kForm, kE8>(a, stream);
         case 5: return launch_tiled<TileNarrow64, kForm, kE8>(a, stream);
         case 6: return launch_tiled<TileNarrow32, kForm, kE8>(a, stream);
+        case 7: return launch_tiled<TileLargeT, kForm, kE8>(a, stream);
         default: return launch_tiled<TileLarge, kForm, kE8>(a, stream);
     }
 }
@@ -728,7 +738,7 @@ hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
         switch (form) {
             case Form::Dense: return launch_dense<Form::Dense, true>(a, stream);
             case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous, true>(a, stream);
-            case Form::Masked: return launch_tiled<TileMasked, Form::Masked, true>(a, stream);
+            case Form::Masked: return launch_tiled<TileLargeT, Form::Masked, true>(a, stream);
             default: return hipErrorInvalidValue;
         }
     }

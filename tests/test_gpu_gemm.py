@@ -101,7 +101,7 @@ def test_dense_parity(orc, M, N, K):
     _check_full(orc, dense_case(M, N, K, seed=M * 7 + N + K, name=f"dense_{M}x{N}x{K}"))
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32"])
+@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32", "256x256t"])
 @pytest.mark.parametrize("M,N,K", [(300, 488, 384), (512, 448, 256), (40, 200, 128)])
 def test_dense_tile_shapes(orc, monkeypatch, tile, M, N, K):
     # every dense tile shape on ragged and exact sizes: several tiles, a
