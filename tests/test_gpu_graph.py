@@ -1,0 +1,61 @@
+"""The GEMM entry points inside a captured HIP graph: each replay, with the
+program's own eager work and synchronizations between replays, must leave
+exactly what an eager call leaves (the entry points allocate, synchronize
+and memset nothing, so they can be captured)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_gemm_amd as dg
+from fp8_block_scaled_gemm_amd.inputs import dense_case, masked_case
+from tests.gpu_util import SENTINEL, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(orc, case):
+    K = case.K
+    qa, sa = orc.quantize_per_token(case.x_a.numpy().reshape(-1, K))
+    xb = case.x_b.numpy()
+    if xb.ndim == 2:
+        qb, sb = orc.quantize_per_block(xb)
+    else:
+        parts = [orc.quantize_per_block(np.ascontiguousarray(xb[g])) for g in range(xb.shape[0])]
+        qb = np.stack([p[0] for p in parts]); sb = np.stack([p[1] for p in parts])
+    qa = qa.reshape(case.x_a.shape)
+    sa = sa.reshape(*case.x_a.shape[:-1], K // 128)
+    return to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
+
+
+@pytest.mark.parametrize("form", ["dense", "masked"])
+def test_graph_replays_match_eager(orc, form):
+    if form == "dense":
+        case = dense_case(300, 520, 768, seed=91)
+        call = dg.dg_fp8_gemm_nt
+        shape = (case.M, case.N)
+    else:
+        case = masked_case(3, 200, 264, 640, 92, masked=[150, 0, 200])
+        call = dg.dg_fp8_gemm_grouped_masked
+        shape = (case.G, case.M, case.N)
+    A, SA, B, SB = _operands(orc, case)
+    extra = (to_dev(case.masked_m.numpy()),) if form == "masked" else ()
+
+    eager = torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda")
+    call(A, SA, B, SB, eager, *extra)
+    torch.cuda.synchronize()
+
+    out = torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(A, SA, B, SB, out, *extra)
+    other = torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda")
+    for rep in range(3):
+        out.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        # eager work between replays, on other buffers
+        call(A, SA, B, SB, other, *extra)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
