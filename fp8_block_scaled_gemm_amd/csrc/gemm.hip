@@ -44,7 +44,7 @@ namespace dg {
 constexpr int kNumXcds = 8;
 
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_, bool ROW_SKIP_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
 struct TileConfig {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -53,9 +53,6 @@ struct TileConfig {
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // rows / cols per wave
     static constexpr int TM = WM / 16, TN = WN / 16;            // 16x16 sub-tiles per wave
     static constexpr int kGroupM = GROUP_M_;                    // m-blocks per raster group
-    // skip the MFMAs of sub-tile rows past the tile's valid rows, a quarter
-    // of the wave tile at a time (worth it where tiles are often partial)
-    static constexpr bool kRowSkip = ROW_SKIP_;
     // one wave-wide direct load fills 1 KiB (8 rows) of a stage; waves take
     // the 8-row groups round-robin (the B slab may end part way round)
     static constexpr int kLoadsA = BM / 8 / kWaves;
@@ -412,8 +409,6 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     const int chunk_lo = (lg ^ (lr & 7)) << 4, chunk_hi = ((lg + 4) ^ (lr & 7)) << 4;
     const int fragA = (16 * wm + lr) * 128, fragB = (wcol + lr) * 128;
     const int srow = 16 * wm + lr;
-    // sub-tile rows of this wave that hold valid rows; the others are skipped
-    const int vsub = (ti.valid - 16 * wm + kRowStep - 1) / kRowStep;
     // column-scale block of sub-tile j, relative to the tile's first one
     int sblk[T::TN];
 #pragma unroll
@@ -466,13 +461,9 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
                 acc[i][j] += (s_a_ * s_b_[T::kOneScaleB ? 0 : j]) * mfma_block(bf_use[j], af_);   \
         }                                                                                         \
     } while (0)
-    // With kRowSkip, a quarter of the sub-tile rows runs only when it holds
-    // valid rows: one uniform branch per quarter.
+    // one quarter of the wave tile's sub-tile rows
 #define DG_QUARTER(bf_use, kb_, st_, q_)                                                          \
-    do {                                                                                          \
-        if (!T::kRowSkip || (q_) == 0 || vsub > (q_) * (T::TM / 4))                               \
-            DG_ROWS(bf_use, kb_, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4));             \
-    } while (0)
+    DG_ROWS(bf_use, kb_, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4))
 
     // One K block kb_ on stages st_ (= kb_ & 1), in two halves separated by
     // a barrier.  The step starts by reading its B fragments (B slab of kb_);
@@ -636,28 +627,28 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 }
 
 // 256x256 tiles, 8 waves of 128x64 (two per SIMD).
-using TileLarge = TileConfig<256, 256, 2, 4, 4, false>;
+using TileLarge = TileConfig<256, 256, 2, 4, 4>;
 // Narrower dense tiles, 8 waves of 64x112 / 64x96: fewer idle CUs in the
 // last round of tiles when N is not a good multiple of 256.
-using TileWide224 = TileConfig<256, 224, 4, 2, 4, false>;
-using TileWide192 = TileConfig<256, 192, 4, 2, 4, false>;
+using TileWide224 = TileConfig<256, 224, 4, 2, 4>;
+using TileWide192 = TileConfig<256, 192, 4, 2, 4>;
 // 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
 // also the dense shape for few rows.
-using TileRows128 = TileConfig<128, 256, 2, 4, 8, false>;
+using TileRows128 = TileConfig<128, 256, 2, 4, 8>;
 // Tiles for few rows (decode-sized M), 4 waves each (64x64, 64x32, 64x16):
 // such a launch is bound by how many bytes of B are in flight (each tile
 // keeps about 1.5 K blocks of loads outstanding), so narrower tiles, more of
 // them, stream B faster.
-using TileSmall = TileConfig<128, 128, 2, 2, 8, false>;
+using TileSmall = TileConfig<128, 128, 2, 2, 8>;
 // 256x256 tiles, 8 waves of 64x128: each A fragment feeds eight MFMAs.  Used
 // with power-of-two scales (without promotion it fits the registers: 231
 // VGPRs; the fp32-scale kernel spills with it).
-using TileLargeT = TileConfig<256, 256, 4, 2, 4, false>;
-using TileNarrow64 = TileConfig<128, 64, 2, 2, 8, false>;
-using TileNarrow32 = TileConfig<128, 32, 2, 2, 8, false>;
+using TileLargeT = TileConfig<256, 256, 4, 2, 4>;
+using TileNarrow64 = TileConfig<128, 64, 2, 2, 8>;
+using TileNarrow32 = TileConfig<128, 32, 2, 2, 8>;
 // Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
 // MFMAs of invalid rows does not shorten them.
-using TileMasked = TileConfig<256, 256, 2, 4, 4, false>;
+using TileMasked = TileConfig<256, 256, 2, 4, 4>;
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
