@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -41,6 +42,9 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
+    # Each compiler writes its messages to a log file, not a pipe: a pipe
+    # nobody drains blocks a compiler with many warnings while another one is
+    # being waited for.
     procs = []
     objs = []
     for src in SOURCES:
@@ -49,13 +53,16 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
         cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        if len([p for p in procs if p[1].poll() is None]) >= jobs:
-            procs[-jobs][1].wait()
+        log = open(obj + ".log", "w+")
+        procs.append((src, subprocess.Popen(cmd, stdout=log, stderr=subprocess.STDOUT), log))
+        while len([p for p in procs if p[1].poll() is None]) >= jobs:
+            time.sleep(0.05)
     failed = []
-    for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+    for src, p, log in procs:
+        p.wait()
+        log.seek(0)
+        text = log.read()
+        log.close()
         # hipcc's host pass does not know the packed-fp32 target feature
         lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip()]
         if p.returncode != 0:
