@@ -134,6 +134,39 @@ def test_contiguous_out_of_range_ids_are_padding(orc):
     _check_full(orc, case)
 
 
+@pytest.mark.parametrize("sizes", [
+    [1, 128, 100, 128, 50, 128, 127],   # every 256-row tile holds two groups
+    [128, 0, 128, 128, 128, 0, 5],      # split, whole and ragged-last tiles
+    [256, 130, 126, 300],               # a tile holds the ends of two groups
+])
+def test_contiguous_split_tiles(orc, sizes):
+    # 256-row tiles whose two 128-row blocks carry different groups: one
+    # workgroup per block, each with its own group's B
+    _check_full(orc, contiguous_case(len(sizes), 264, 384, seed=len(sizes) + sum(sizes),
+                                     sizes=sizes))
+
+
+def test_contiguous_mixed_block_routes_largest_id(orc):
+    # a 128-row block that mixes two valid ids routes only the rows of the
+    # larger one; the other rows of that block stay untouched
+    case = contiguous_case(3, 136, 256, seed=21, sizes=[128, 128, 128])
+    lay = case.layout.clone()
+    lay[140:150] = 0    # block 1 (group 1) with some rows of group 0
+    lay[260:270] = 2    # block 2 is group 2 already: no change in routing
+    lay[10:20] = 2      # block 0 (group 0) with rows of group 2: group 2 wins
+    case.layout = lay
+    qa, sa, qb, sb = _prepared(orc, case)
+    got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
+    ref = _oracle_full(orc, case, qa, sa, qb, sb).reshape(-1, case.N)
+    routed = np.zeros(case.M, bool)
+    routed[10:20] = True            # block 0: only the group-2 rows
+    routed[128:140] = True          # block 1: group-1 rows only
+    routed[150:256] = True
+    routed[256:384] = True          # block 2: all group 2
+    assert (got[~routed] == 0xFFFF).all()
+    assert_close_bf16(got[routed], ref[routed], "mixed blocks")
+
+
 def test_contiguous_all_padding_leaves_d_untouched(orc):
     case = contiguous_case(2, 64, 256, seed=13, sizes=[0, 0])
     case.layout = torch.full((256,), -1, dtype=torch.int32)
