@@ -117,12 +117,30 @@ def test_dense_parity_scaled_rows(orc):
     _check_full(orc, case)
 
 
-@pytest.mark.parametrize("sizes", [[100, 0, 260], [128, 1, 255, 3], [0, 0]])
+@pytest.mark.parametrize("sizes", [[100, 0, 260], [128, 1, 255, 3]])
 def test_contiguous_parity(orc, sizes):
     case = contiguous_case(len(sizes), 264, 512, seed=sum(sizes) + 1, sizes=sizes)
-    if case.M == 0:
-        pytest.skip("no rows")
     _check_full(orc, case)
+
+
+def test_zero_rows_are_a_no_op(orc):
+    """M = 0 (dense), M_sum = 0 (contiguous) and M_max = 0 (masked) enqueue
+    nothing and return success; a neighbouring buffer stays untouched."""
+    dev = torch.device("cuda:0")
+    K, N, G = 256, 64, 2
+    A = torch.zeros((0, K), dtype=torch.uint8, device=dev)
+    SA = torch.zeros((0, K // 128), dtype=torch.float32, device=dev)
+    B = torch.zeros((G, N, K), dtype=torch.uint8, device=dev)
+    SB = torch.ones((G, N // 128 + 1, K // 128), dtype=torch.float32, device=dev)
+    guard = torch.full((16, N), SENTINEL, dtype=torch.int16, device=dev)
+    D = guard[:0]
+    dg.dg_fp8_gemm_nt(A, SA, B[0], SB[0], D)
+    dg.dg_fp8_gemm_grouped_contiguous(A, SA, B, SB, D, torch.zeros(0, dtype=torch.int32, device=dev))
+    dg.dg_fp8_gemm_grouped_masked(A.reshape(G, 0, K), SA.reshape(G, 0, K // 128), B, SB,
+                                  guard[:0].reshape(G, 0, N),
+                                  torch.zeros(G, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert (guard.cpu().numpy().view(np.uint16) == 0xFFFF).all()
 
 
 def test_contiguous_out_of_range_ids_are_padding(orc):
