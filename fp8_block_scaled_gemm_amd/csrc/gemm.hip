@@ -632,6 +632,7 @@ using TileLarge = TileConfig<256, 256, 2, 4, 4>;
 // last round of tiles when N is not a good multiple of 256.
 using TileWide224 = TileConfig<256, 224, 4, 2, 4>;
 using TileWide192 = TileConfig<256, 192, 4, 2, 4>;
+using TileWide160 = TileConfig<256, 160, 4, 2, 4>;
 // 128x256 tiles, 8 waves of 64x64: contiguous groups are padded to 128 rows;
 // also the dense shape for few rows.
 using TileRows128 = TileConfig<128, 256, 2, 4, 8>;
@@ -663,15 +664,15 @@ static int device_cus() {
     return n;
 }
 
-// DG_FP8_DENSE_TILE=256x256|256x224|256x192|128x256|128x128|128x64|128x32 pins the dense tile
+// DG_FP8_DENSE_TILE=256x256|256x224|256x192|256x160|128x256|128x128|128x64|128x32|256x256t pins the dense tile
 // shape (for tests and tuning; read at every call); -1 when unset or not
 // one of these.
 static int forced_dense_shape() {
     const char* e = getenv("DG_FP8_DENSE_TILE");
     if (!e) return -1;
     const char* names[] = {"256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32",
-                           "256x256t"};
-    for (int i = 0; i < 8; ++i)
+                           "256x256t", "256x160"};
+    for (int i = 0; i < 9; ++i)
         if (strcmp(e, names[i]) == 0) return i;
     return -1;
 }
@@ -687,11 +688,13 @@ static int forced_dense_shape() {
 // 128 x 7168 x 2048: 13.7 us against 17.7 with 128x128 and 24 with 128x256).
 template <Form kForm, bool kE8>
 static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
-    struct Shape { int bm, bn; double rel; };
+    struct Shape { int bm, bn; double rel; int id; };
     // per-area costs from measured loop cycles per K block (256x256: 3.43k,
-    // 256x224: 3.42k, 256x192: 2.93k, 128x256: 2.08k cycles)
-    static const Shape kShapes[] = {{256, 256, 1.00}, {256, 224, 1.15}, {256, 192, 1.15},
-                                    {128, 256, 1.22}};
+    // 256x224: 3.42k, 256x192: 2.93k, 128x256: 2.08k cycles); 256x160 from
+    // whole launches of 4096 x 2112 x 7168, one round of tiles each: 86.2 us
+    // against 91.6 us with 256x192
+    static const Shape kShapes[] = {{256, 256, 1.00, 0}, {256, 224, 1.15, 1}, {256, 192, 1.15, 2},
+                                    {128, 256, 1.22, 3}, {256, 160, 1.30, 8}};
     const int64_t cus = device_cus();
     const int forced = forced_dense_shape();
     int best = forced;
@@ -699,13 +702,13 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     if (best < 0 && 2 * tiles_large <= cus) best = 6;
     if (best < 0) {
         double best_cost = 0;
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < (int)(sizeof(kShapes) / sizeof(kShapes[0])); ++i) {
             const Shape& sh = kShapes[i];
             const int64_t tiles = ((a.rows + sh.bm - 1) / sh.bm) * ((a.N + sh.bn - 1) / sh.bn);
             const double cost = (double)((tiles + cus - 1) / cus) * sh.bm * sh.bn * sh.rel;
             if (i == 0 || cost < best_cost) {
                 best_cost = cost;
-                best = i;
+                best = sh.id;
             }
         }
         // with power-of-two scales the 64x128 wave layout of 256x256 is the
@@ -720,6 +723,7 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
         case 5: return launch_tiled<TileNarrow64, kForm, kE8>(a, stream);
         case 6: return launch_tiled<TileNarrow32, kForm, kE8>(a, stream);
         case 7: return launch_tiled<TileLargeT, kForm, kE8>(a, stream);
+        case 8: return launch_tiled<TileWide160, kForm, kE8>(a, stream);
         default: return launch_tiled<TileLarge, kForm, kE8>(a, stream);
     }
 }

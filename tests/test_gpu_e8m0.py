@@ -150,7 +150,7 @@ def _check_full(orc, case):
         assert_close_bf16(got[rows], ref[rows], case.name)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32", "256x256t"])
+@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "256x160", "128x256", "128x128", "128x64", "128x32", "256x256t"])
 @pytest.mark.parametrize("M,N,K", [(300, 712, 1024), (129, 136, 256), (64, 528, 384),
                                    (1, 8, 128), (257, 264, 1152)])
 def test_dense_e8m0_parity(orc, monkeypatch, tile, M, N, K):

@@ -101,7 +101,7 @@ def test_dense_parity(orc, M, N, K):
     _check_full(orc, dense_case(M, N, K, seed=M * 7 + N + K, name=f"dense_{M}x{N}x{K}"))
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32", "256x256t"])
+@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "256x160", "128x256", "128x128", "128x64", "128x32", "256x256t"])
 @pytest.mark.parametrize("M,N,K", [(300, 488, 384), (512, 448, 256), (40, 200, 128)])
 def test_dense_tile_shapes(orc, monkeypatch, tile, M, N, K):
     # every dense tile shape on ragged and exact sizes: several tiles, a
@@ -242,13 +242,13 @@ def test_epilogue_rounding_is_exact(orc, monkeypatch):
     assert ties.sum() > 1000
     ref = orc.gemm_nt(qa, sa, qb, sb)
     case = dense_case(M, N, K, seed=0)
-    for tile in ("256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32"):
+    for tile in ("256x256", "256x224", "256x192", "256x160", "128x256", "128x128", "128x64", "128x32"):
         monkeypatch.setenv("DG_FP8_DENSE_TILE", tile)
         got = _run(case, qa, sa, qb, sb).reshape(M, N)
         assert np.array_equal(got, ref), tile
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "128x256", "128x128", "128x64", "128x32", None])
+@pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "256x160", "128x256", "128x128", "128x64", "128x32", None])
 @pytest.mark.parametrize("M,N,K", [(300, 488, 384), (64, 256, 128), (512, 520, 256)])
 def test_dense_acc_parity(orc, monkeypatch, tile, M, N, K):
     """D = bf16(C + dense sum) against the oracle; C of the product's size
