@@ -158,8 +158,12 @@ def gemm_call(case, dg, t):
 
 def time_quantize(dg, t, case, reps=20):
     """Average time of the per-token quantization of A (the activation side,
-    re-done every step in use), from fp32 and from bf16 input, with HIP
-    events; reported beside the GEMM."""
+    re-done every step in use), from fp32 and from bf16 input, and of the
+    per-block quantization of one B matrix; reported beside the GEMM.  Each
+    is timed with HIP events around one replay of a captured graph of `reps`
+    calls: these kernels take a few microseconds, about what one call through
+    the Python binding costs on the host, so eager launches would time the
+    host."""
     import torch
     x = t["x_a"].reshape(-1, case.K)
     xb = x.to(torch.bfloat16)
@@ -169,10 +173,16 @@ def time_quantize(dg, t, case, reps=20):
     def timed(fn, src, q_, s_):
         for _ in range(3):
             fn(src, q_, s_)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                fn(src, q_, s_)
+        graph.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            fn(src, q_, s_)
+        graph.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
