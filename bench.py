@@ -10,7 +10,8 @@ them from one step to the next.
 Prints one JSON line:
   value        TFLOPS over the timed steps (2*rows*N*K per step / wall time)
   roofline     the GEMM kernel against the dense FP8 MFMA peak (or HBM for
-               bandwidth-bound workloads), from HIP events around each launch
+               bandwidth-bound workloads), from HIP events on the launch
+               stream around the timed graph replay (one GEMM per step)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -326,23 +327,20 @@ def main():
         # The K timed steps are one captured HIP graph (the entry points
         # allocate, synchronize and memset nothing, so they capture), which
         # takes the host's per-call launch cost out of the step rate.  The
-        # per-kernel duration comes from the same K steps launched eagerly
-        # with events around each launch.
-        for i in range(args.steps):
-            starts[i].record(stream)
-            gemm_call(case, dg, sets[i % copies])
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+        # per-kernel duration is the HIP-event time of that replay on the
+        # launch stream over K (the graph holds one GEMM kernel per step).
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(args.steps):
                 gemm_call(case, dg, sets[i % copies])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        starts[0].record(stream)
         graph.replay()
+        ends[0].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        kernel_ms = starts[0].elapsed_time(ends[0]) / args.steps
         # the replay must leave what an eager call writes, bit for bit (rows
         # a call does not route stay as they were in both)
         replayed = sets[0]["D"].clone()
