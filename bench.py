@@ -13,6 +13,7 @@ Prints one JSON line:
                bandwidth-bound workloads), from HIP events on the launch
                stream around the timed graph replay (one GEMM per step)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
+  same_buffer  the same steps on one input set (warm caches), for comparison
 """
 from __future__ import annotations
 
@@ -155,6 +156,26 @@ def gemm_call(case, dg, t):
         dg.dg_fp8_gemm_grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
     else:
         dg.dg_fp8_gemm_grouped_masked(t["A"], t["sa"], t["B"], t["sb"], t["D"], t["aux"])
+
+
+def same_buffer_rate(case, dg, inputs, steps, flop):
+    """The same K steps on one input set (warm: operands may stay in the
+    last-level cache between steps), as a captured graph, for comparison
+    with the rotated-input figure that `value` reports."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            gemm_call(case, dg, inputs)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"kernel_us": round(us, 2), "TFLOPS": round(flop / (us * 1e-6) / 1e12, 1)}
 
 
 def time_quantize(dg, t, case, reps=20):
@@ -366,6 +387,7 @@ def main():
     roof["algorithmic_flop"] = flop
     roof["algorithmic_bytes"] = byts
 
+    warm = None if args.no_graph else same_buffer_rate(case, dg, sets[0], args.steps, flop)
     quant = time_quantize(dg, base, case)
     cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
 
@@ -380,6 +402,7 @@ def main():
                    "rotated_input_sets": copies},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "same_buffer": warm,
         "quantize": quant,
     }
     print(json.dumps(line), flush=True)
