@@ -19,6 +19,8 @@ bool product_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
 dg_status check_nk(int64_t N, int64_t K) {
     if (N <= 0 || N % 8 != 0) return DG_ERR_SHAPE;
     if (K <= 0 || K % 128 != 0) return DG_ERR_SHAPE;
+    // a tile's rows (up to 256) of K bytes are addressed with 32-bit offsets
+    if (K >= (int64_t(1) << 24)) return DG_ERR_SHAPE;
     if (!product_ok(N, K)) return DG_ERR_SHAPE;
     if (N > 0x7fffffffLL || K > 0x7fffffffLL) return DG_ERR_SHAPE;
     return DG_OK;

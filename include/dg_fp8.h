@@ -60,7 +60,8 @@ typedef enum {
  *   D  [M][N]  bf16 bits (output)
  * Sizes: M >= 0 (0 enqueues nothing), N > 0 with N % 8 == 0 (the page's
  * kernel asserts N % 8), K > 0 with K % 128 == 0 (its static check fixes the
- * 128-channel K block).  All of M*K, N*K, M*N must be below 2^62. */
+ * 128-channel K block) and K < 2^24 (a tile's rows of K bytes are addressed
+ * with 32-bit offsets).  All of M*K, N*K, M*N must be below 2^62. */
 dg_status dg_fp8_gemm_nt(const uint8_t* A, const float* sa,
                          const uint8_t* B, const float* sb,
                          uint16_t* D, int64_t M, int64_t N, int64_t K,

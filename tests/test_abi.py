@@ -77,6 +77,7 @@ def test_dense_rejects_bad_shapes(lib):
     assert _gemm_nt(lib, N=0) == DG_ERR_SHAPE
     assert _gemm_nt(lib, M=-1) == DG_ERR_SHAPE
     assert _gemm_nt(lib, M=1 << 40, N=1 << 30) == DG_ERR_SHAPE
+    assert _gemm_nt(lib, K=1 << 24) == DG_ERR_SHAPE          # 32-bit tile offsets
 
 
 def test_dense_rejects_null_and_misaligned(lib):
