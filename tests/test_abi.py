@@ -169,3 +169,12 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liborc" not in text, f
+
+
+def test_binding_refuses_tensors_on_two_devices():
+    import torch
+    import fp8_block_scaled_gemm_amd as dg
+    a, b = torch.zeros(4), torch.zeros(4, device="meta")
+    assert dg._device_of(a, a) == a.device
+    with pytest.raises(ValueError, match="one device"):
+        dg._device_of(a, b)
