@@ -140,7 +140,8 @@ def dg_fp8_gemm_nt(A, sa, B, sb, D):
     _check(A, "A"); _check(B, "B", shape=(N, K))
     _check(sa, "sa", torch.float32, (M, KB)); _check(sb, "sb", torch.float32, (NB, KB))
     _check(D, "D", _D_TYPES, (M, N))
-    _call(_device_of(A, sa, B, sb, D), "dg_fp8_gemm_nt", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D), "dg_fp8_gemm_nt",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
           D.data_ptr(), M, N, K, _stream_ptr(D))
     return D
 
@@ -155,7 +156,8 @@ def dg_fp8_gemm_nt_acc(A, sa, B, sb, C, D):
     _check(sa, "sa", torch.float32, (M, KB)); _check(sb, "sb", torch.float32, (NB, KB))
     _check(C, "C", torch.float32, (M, N))
     _check(D, "D", _D_TYPES, (M, N))
-    _call(_device_of(A, sa, B, sb, C, D), "dg_fp8_gemm_nt_acc", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+    _call(_device_of(A, sa, B, sb, C, D), "dg_fp8_gemm_nt_acc",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
           C.data_ptr(), D.data_ptr(), M, N, K, _stream_ptr(D))
     return D
 
@@ -171,7 +173,8 @@ def dg_fp8_gemm_grouped_contiguous(A, sa, B, sb, D, grouped_layout):
     _check(sa, "sa", torch.float32, (M_sum, KB)); _check(sb, "sb", torch.float32, (G, NB, KB))
     _check(D, "D", _D_TYPES, (M_sum, N))
     _check(grouped_layout, "grouped_layout", torch.int32, (M_sum,))
-    _call(_device_of(A, sa, B, sb, D, grouped_layout), "dg_fp8_gemm_grouped_contiguous", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D, grouped_layout), "dg_fp8_gemm_grouped_contiguous",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(),
           sb.data_ptr(), D.data_ptr(), grouped_layout.data_ptr(), M_sum, N, K, G, _stream_ptr(D))
     return D
 
@@ -187,7 +190,8 @@ def dg_fp8_gemm_grouped_masked(A, sa, B, sb, D, masked_m):
     _check(sa, "sa", torch.float32, (G, M_max, KB)); _check(sb, "sb", torch.float32, (G, NB, KB))
     _check(D, "D", _D_TYPES, (G, M_max, N))
     _check(masked_m, "masked_m", torch.int32, (G,))
-    _call(_device_of(A, sa, B, sb, D, masked_m), "dg_fp8_gemm_grouped_masked", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D, masked_m), "dg_fp8_gemm_grouped_masked",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(),
           sb.data_ptr(), D.data_ptr(), masked_m.data_ptr(), G, M_max, N, K, _stream_ptr(D))
     return D
 
@@ -202,7 +206,8 @@ def dg_quantize_fp8_per_token(x, q=None, s=None):
         s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
     q = _bytes(q, "q")
     _check(q, "q", shape=(M, K)); _check(s, "s", torch.float32, (M, K // 128))
-    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
+    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token",
+          x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s
 
@@ -217,7 +222,8 @@ def dg_quantize_fp8_per_token_bf16(x, q=None, s=None):
         s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
     q = _bytes(q, "q")
     _check(q, "q", shape=(M, K)); _check(s, "s", torch.float32, (M, K // 128))
-    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token_bf16", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
+    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token_bf16",
+          x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s
 
@@ -233,7 +239,8 @@ def dg_quantize_fp8_per_block(x, q=None, s=None):
         s = torch.empty((NB, K // 128), dtype=torch.float32, device=x.device)
     q = _bytes(q, "q")
     _check(q, "q", shape=(N, K)); _check(s, "s", torch.float32, (NB, K // 128))
-    _call(_device_of(x, q, s), "dg_quantize_fp8_per_block", x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
+    _call(_device_of(x, q, s), "dg_quantize_fp8_per_block",
+          x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s
 
@@ -254,7 +261,8 @@ def dg_fp8_gemm_nt_e8m0(A, sa, B, sb, D):
     _check(A, "A"); _check(B, "B", shape=(N, K))
     _check(sa, "sa", torch.uint8, (M, SP)); _check(sb, "sb", torch.uint8, (NB, SP))
     _check(D, "D", _D_TYPES, (M, N))
-    _call(_device_of(A, sa, B, sb, D), "dg_fp8_gemm_nt_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D), "dg_fp8_gemm_nt_e8m0",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
           D.data_ptr(), M, N, K, _stream_ptr(D))
     return D
 
@@ -269,7 +277,8 @@ def dg_fp8_gemm_grouped_contiguous_e8m0(A, sa, B, sb, D, grouped_layout):
     _check(sa, "sa", torch.uint8, (M_sum, SP)); _check(sb, "sb", torch.uint8, (G, NB, SP))
     _check(D, "D", _D_TYPES, (M_sum, N))
     _check(grouped_layout, "grouped_layout", torch.int32, (M_sum,))
-    _call(_device_of(A, sa, B, sb, D, grouped_layout), "dg_fp8_gemm_grouped_contiguous_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D, grouped_layout), "dg_fp8_gemm_grouped_contiguous_e8m0",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(),
           sb.data_ptr(), D.data_ptr(), grouped_layout.data_ptr(), M_sum, N, K, G, _stream_ptr(D))
     return D
 
@@ -284,7 +293,8 @@ def dg_fp8_gemm_grouped_masked_e8m0(A, sa, B, sb, D, masked_m):
     _check(sa, "sa", torch.uint8, (G, M_max, SP)); _check(sb, "sb", torch.uint8, (G, NB, SP))
     _check(D, "D", _D_TYPES, (G, M_max, N))
     _check(masked_m, "masked_m", torch.int32, (G,))
-    _call(_device_of(A, sa, B, sb, D, masked_m), "dg_fp8_gemm_grouped_masked_e8m0", A.data_ptr(), sa.data_ptr(), B.data_ptr(),
+    _call(_device_of(A, sa, B, sb, D, masked_m), "dg_fp8_gemm_grouped_masked_e8m0",
+          A.data_ptr(), sa.data_ptr(), B.data_ptr(),
           sb.data_ptr(), D.data_ptr(), masked_m.data_ptr(), G, M_max, N, K, _stream_ptr(D))
     return D
 
@@ -301,7 +311,8 @@ def dg_quantize_fp8_per_token_e8m0(x, q=None, s=None):
         s = torch.zeros((M, SP), dtype=torch.uint8, device=x.device)
     q = _bytes(q, "q")
     _check(q, "q", shape=(M, K)); _check(s, "s", torch.uint8, (M, SP))
-    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token_e8m0", x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
+    _call(_device_of(x, q, s), "dg_quantize_fp8_per_token_e8m0",
+          x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s
 
@@ -317,6 +328,7 @@ def dg_quantize_fp8_per_block_e8m0(x, q=None, s=None):
         s = torch.zeros((NB, SP), dtype=torch.uint8, device=x.device)
     q = _bytes(q, "q")
     _check(q, "q", shape=(N, K)); _check(s, "s", torch.uint8, (NB, SP))
-    _call(_device_of(x, q, s), "dg_quantize_fp8_per_block_e8m0", x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
+    _call(_device_of(x, q, s), "dg_quantize_fp8_per_block_e8m0",
+          x.data_ptr(), N, K, q.data_ptr(), s.data_ptr(),
           _stream_ptr(x))
     return q, s

@@ -59,3 +59,31 @@ def test_graph_replays_match_eager(orc, form):
         call(A, SA, B, SB, other, *extra)
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
+
+
+@pytest.mark.parametrize("kind", ["per_token", "per_token_bf16", "per_block",
+                                  "per_token_e8m0", "per_block_e8m0"])
+def test_quantizer_graph_replays_match_eager(kind):
+    # bench.py times the quantizers as captured graphs: every replay, with
+    # eager work between replays, must give the eager call's codes and scales
+    g = torch.Generator().manual_seed(93)
+    x = torch.randn(260, 640, generator=g).cuda()
+    if kind.endswith("bf16"):
+        x = x.to(torch.bfloat16)
+    fn = getattr(dg, "dg_quantize_fp8_" + kind)
+    eq, es = fn(x)
+    torch.cuda.synchronize()
+    q, s = torch.empty_like(eq), torch.empty_like(es)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn(x, q, s)
+    for rep in range(3):
+        q.fill_(0)
+        s.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, eq) and torch.equal(s, es), f"replay {rep} differs from the eager call"
+        oq, os_ = fn(x)          # eager work between replays, on other buffers
+        torch.cuda.synchronize()
+        assert torch.equal(oq, eq) and torch.equal(os_, es)
