@@ -169,6 +169,11 @@ def test_dense_e8m0_wide_exponents(orc):
     _check_full(orc, case)
 
 
+def test_grouped_e8m0_with_one_k_block(orc):
+    _check_full(orc, contiguous_case(3, 136, 128, 33, sizes=[130, 0, 256]))
+    _check_full(orc, masked_case(3, 192, 264, 128, 34, masked=[192, 5, 0]))
+
+
 @pytest.mark.parametrize("sizes", [[100, 0, 260], [128, 1, 255, 3]])
 def test_contiguous_e8m0_parity(orc, sizes):
     _check_full(orc, contiguous_case(len(sizes), 264, 384, 7, sizes=sizes))

@@ -143,6 +143,13 @@ def test_zero_rows_are_a_no_op(orc):
     assert (guard.cpu().numpy().view(np.uint16) == 0xFFFF).all()
 
 
+def test_grouped_forms_with_one_k_block(orc):
+    # K = 128: the pipeline's second prologue block and every refill are
+    # empty loads
+    _check_full(orc, contiguous_case(3, 136, 128, seed=31, sizes=[130, 0, 256]))
+    _check_full(orc, masked_case(3, 192, 264, 128, seed=32, masked=[192, 5, 0]))
+
+
 def test_contiguous_out_of_range_ids_are_padding(orc):
     case = contiguous_case(3, 136, 256, seed=12, sizes=[200, 50, 128])
     lay = case.layout.clone()
