@@ -35,6 +35,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -651,16 +652,22 @@ using TileNarrow32 = TileConfig<128, 32, 2, 2, 8>;
 // MFMAs of invalid rows does not shorten them.
 using TileMasked = TileConfig<256, 256, 2, 4, 4>;
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device.  Host threads may
+// launch concurrently: each slot only ever receives its device's one value,
+// so relaxed atomics suffice.
 static int device_cus() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    const bool slot = dev >= 0 && dev < 64;
+    if (slot) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
         n = 256;
-    if (dev >= 0 && dev < 64) cached[dev] = n;
+    if (slot) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
