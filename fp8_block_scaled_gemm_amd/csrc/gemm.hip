@@ -442,6 +442,7 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
             _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)               \
                 e_b_[j] = eSB_[sblk[j] * 4];                                                      \
             _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                               \
+                if (kForm == Form::Masked && 16 * wm + kRowStep * i >= ti.valid) continue;       \
                 const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);   \
                 const int e_a_ = eSA_[(srow + kRowStep * i) * 4];                                 \
                 _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                 \
@@ -456,6 +457,7 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
         _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)                   \
             s_b_[j] = sSB_[sblk[j] * 4];                                                          \
         _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
+            if (kForm == Form::Masked && 16 * wm + kRowStep * i >= ti.valid) continue;           \
             const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);       \
             const float s_a_ = sSA_[(srow + kRowStep * i) * 4];                                   \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
@@ -648,8 +650,10 @@ using TileSmall = TileConfig<128, 128, 2, 2, 8>;
 using TileLargeT = TileConfig<256, 256, 4, 2, 4>;
 using TileNarrow64 = TileConfig<128, 64, 2, 2, 8>;
 using TileNarrow32 = TileConfig<128, 32, 2, 2, 8>;
-// Masked groups: 256x256 tiles; they stream B from HBM, so skipping the
-// MFMAs of invalid rows does not shorten them.
+// Masked groups: 256x256 tiles.  A wave skips the fragment reads, MFMAs and
+// promotion of its 16-row sub-tile rows that hold no valid row (a uniform
+// branch on the group's count), so tiles of short groups finish early and
+// stop drawing on HBM while the full slabs still stream.
 using TileMasked = TileConfig<256, 256, 2, 4, 4>;
 
 // Compute units of the current device, cached per device.  Host threads may
