@@ -442,7 +442,7 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
             _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)               \
                 e_b_[j] = eSB_[sblk[j] * 4];                                                      \
             _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                               \
-                if (kForm == Form::Masked && 16 * wm + kRowStep * i >= ti.valid) continue;       \
+                if (kSkipRows && 16 * wm + kRowStep * i >= ti.valid) continue;       \
                 const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);   \
                 const int e_a_ = eSA_[(srow + kRowStep * i) * 4];                                 \
                 _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                 \
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
         _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)                   \
             s_b_[j] = sSB_[sblk[j] * 4];                                                          \
         _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
-            if (kForm == Form::Masked && 16 * wm + kRowStep * i >= ti.valid) continue;           \
+            if (kSkipRows && 16 * wm + kRowStep * i >= ti.valid) continue;           \
             const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);       \
             const float s_a_ = sSA_[(srow + kRowStep * i) * 4];                                   \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
@@ -517,10 +517,31 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     lds_barrier();
     DG_ISSUE_AH(1, 1);
 
-    for (int kb = 0; kb < KB; kb += 2) {
-        DG_STEP(kb, 0);
-        if (kb + 1 < KB) DG_STEP(kb + 1, 1);
+#define DG_K_LOOP()                                                                               \
+    for (int kb = 0; kb < KB; kb += 2) {                                                          \
+        DG_STEP(kb, 0);                                                                           \
+        if (kb + 1 < KB) DG_STEP(kb + 1, 1);                                                      \
     }
+    // A masked tile with rows past its group's count runs a copy of the loop
+    // that skips sub-tile rows without a valid row (kSkipRows).  With fp32
+    // scales full tiles keep the branch-free loop, whose schedule is faster;
+    // with E8M0 scales one skipping loop serves every tile (measured faster).
+    if constexpr (kForm == Form::Masked && kE8) {
+        constexpr bool kSkipRows = true;
+        DG_K_LOOP();
+    } else if constexpr (kForm == Form::Masked) {
+        if (ti.valid < T::BM) {
+            constexpr bool kSkipRows = true;
+            DG_K_LOOP();
+        } else {
+            constexpr bool kSkipRows = false;
+            DG_K_LOOP();
+        }
+    } else {
+        constexpr bool kSkipRows = false;
+        DG_K_LOOP();
+    }
+#undef DG_K_LOOP
 #undef DG_STEP
 #undef DG_QUARTER
 #undef DG_ROWS
@@ -650,10 +671,11 @@ using TileSmall = TileConfig<128, 128, 2, 2, 8>;
 using TileLargeT = TileConfig<256, 256, 4, 2, 4>;
 using TileNarrow64 = TileConfig<128, 64, 2, 2, 8>;
 using TileNarrow32 = TileConfig<128, 32, 2, 2, 8>;
-// Masked groups: 256x256 tiles.  A wave skips the fragment reads, MFMAs and
-// promotion of its 16-row sub-tile rows that hold no valid row (a uniform
-// branch on the group's count), so tiles of short groups finish early and
-// stop drawing on HBM while the full slabs still stream.
+// Masked groups: 256x256 tiles.  In a tile with rows past its group's count
+// a wave skips the fragment reads, MFMAs and promotion of its 16-row sub-tile
+// rows that hold no valid row (a uniform branch on the count), so tiles of
+// short groups finish early and stop drawing on HBM while the full slabs
+// still stream; full tiles run the branch-free loop.
 using TileMasked = TileConfig<256, 256, 2, 4, 4>;
 
 // Compute units of the current device, cached per device.  Host threads may
