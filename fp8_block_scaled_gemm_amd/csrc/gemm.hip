@@ -429,7 +429,9 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_
+    // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_;
+    // with kSkipRows (a constexpr flag of the enclosing K loop copy, see
+    // below) rows that hold no valid row of the tile are skipped
 #define DG_ROWS(bf_use, kb_, st_, i0_, i1_)                                                       \
     do {                                                                                          \
         if constexpr (kE8) {                                                                      \
