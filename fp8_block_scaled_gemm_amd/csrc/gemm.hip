@@ -623,7 +623,9 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
             bool ok = row < ti.valid && col < N;
             if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
             const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
-            if (ok) *reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col) = v;
+            // D is written once and not read back here: non-temporal stores keep
+            // it from evicting operand slabs that later tiles still read
+            if (ok) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col));
         }
     }
 }
