@@ -181,25 +181,37 @@ def same_buffer_rate(case, dg, inputs, steps, flop):
 def time_quantize(dg, t, case, reps=20):
     """Average time of the per-token quantization of A (the activation side,
     re-done every step in use), from fp32 and from bf16 input, and of the
-    per-block quantization of one B matrix; reported beside the GEMM.  Each
-    is timed with HIP events around one replay of a captured graph of `reps`
-    calls: these kernels take a few microseconds, about what one call through
-    the Python binding costs on the host, so eager launches would time the
-    host."""
+    per-block quantization of one B matrix; reported beside the GEMM.
+
+    Each is timed with HIP events around one replay of a captured graph of
+    `reps` calls (these kernels take a few microseconds, about what one call
+    through the Python binding costs on the host, so eager launches would
+    time the host).  The calls rotate over distinct input and output buffers
+    totalling more than 512 MiB, so every call reads its input from HBM and
+    not from the 256 MiB last-level cache."""
     import torch
     x = t["x_a"].reshape(-1, case.K)
-    xb = x.to(torch.bfloat16)
-    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    s = torch.empty((x.shape[0], case.K // 128), dtype=torch.float32, device=x.device)
+    w = t["x_b"].reshape(-1, case.K) if t["x_b"].dim() == 2 else t["x_b"][0]
+    KB, SP = case.K // 128, dg.e8m0_pitch(case.K // 128)
+    NB = (w.shape[0] + 127) // 128
 
-    def timed(fn, src, q_, s_):
-        for _ in range(3):
-            fn(src, q_, s_)
+    def buffers(src, s_shape, s_dtype, in_dtype):
+        """Copies of (input, codes, scales), enough of them to exceed the
+        rotation size."""
+        src = src.to(in_dtype)
+        one = src.numel() * (src.element_size() + 1) + 4 * s_shape[0] * s_shape[1]
+        n = max(2, -(-ROTATE_BYTES // one))
+        return [(src.clone(), torch.empty(src.shape, dtype=torch.uint8, device=src.device),
+                 torch.zeros(s_shape, dtype=s_dtype, device=src.device)) for _ in range(n)]
+
+    def timed(fn, bufs):
+        for i in range(3):
+            fn(*bufs[i % len(bufs)])
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for _ in range(reps):
-                fn(src, q_, s_)
+            for i in range(reps):
+                fn(*bufs[i % len(bufs)])
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -207,22 +219,23 @@ def time_quantize(dg, t, case, reps=20):
         graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / reps, len(bufs)
 
-    KB, SP = case.K // 128, dg.e8m0_pitch(case.K // 128)
-    s8 = torch.zeros((x.shape[0], SP), dtype=torch.uint8, device=x.device)
-    ms = timed(dg.dg_quantize_fp8_per_token, x, q, s)
-    ms_b = timed(dg.dg_quantize_fp8_per_token_bf16, xb, q, s)
-    ms_e = timed(dg.dg_quantize_fp8_per_token_e8m0, x, q, s8)
-    w = t["x_b"].reshape(-1, case.K) if t["x_b"].dim() == 2 else t["x_b"][0]
-    NB = (w.shape[0] + 127) // 128
-    qw = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    sw = torch.empty((NB, KB), dtype=torch.float32, device=w.device)
-    sw8 = torch.zeros((NB, SP), dtype=torch.uint8, device=w.device)
-    ms_w = timed(dg.dg_quantize_fp8_per_block, w, qw, sw)
-    ms_we = timed(dg.dg_quantize_fp8_per_block_e8m0, w, qw, sw8)
-    byts = x.numel() * 5 + s.numel() * 4
-    byts_b = x.numel() * 3 + s.numel() * 4
+    res = {}
+    tok32 = buffers(x, (x.shape[0], KB), torch.float32, torch.float32)
+    ms, n_tok = timed(dg.dg_quantize_fp8_per_token, tok32)
+    del tok32
+    ms_b, _ = timed(dg.dg_quantize_fp8_per_token_bf16,
+                    buffers(x, (x.shape[0], KB), torch.float32, torch.bfloat16))
+    ms_e, _ = timed(dg.dg_quantize_fp8_per_token_e8m0,
+                    buffers(x, (x.shape[0], SP), torch.uint8, torch.float32))
+    ms_w, n_blk = timed(dg.dg_quantize_fp8_per_block,
+                        buffers(w, (NB, KB), torch.float32, torch.float32))
+    ms_we, _ = timed(dg.dg_quantize_fp8_per_block_e8m0,
+                     buffers(w, (NB, SP), torch.uint8, torch.float32))
+    torch.cuda.empty_cache()
+    byts = x.numel() * 5 + x.shape[0] * KB * 4
+    byts_b = x.numel() * 3 + x.shape[0] * KB * 4
     byts_e = x.numel() * 5 + x.shape[0] * KB
     byts_w = w.numel() * 5 + NB * KB * 4
     byts_we = w.numel() * 5 + NB * KB
@@ -230,13 +243,16 @@ def time_quantize(dg, t, case, reps=20):
     def gbs(b, m):
         return round(b / (m * 1e-3) / 1e9, 1)
 
-    return {"kernel": "quantize_per_token", "rows": int(x.shape[0]), "K": case.K,
-            "us": round(ms * 1e3, 2), "GB/s": gbs(byts, ms),
-            "bf16_input_us": round(ms_b * 1e3, 2), "bf16_input_GB/s": gbs(byts_b, ms_b),
-            "e8m0_us": round(ms_e * 1e3, 2), "e8m0_GB/s": gbs(byts_e, ms_e),
-            "per_block_rows": int(w.shape[0]), "per_block_us": round(ms_w * 1e3, 2),
-            "per_block_GB/s": gbs(byts_w, ms_w),
-            "per_block_e8m0_us": round(ms_we * 1e3, 2), "per_block_e8m0_GB/s": gbs(byts_we, ms_we)}
+    res.update({"kernel": "quantize_per_token", "rows": int(x.shape[0]), "K": case.K,
+                "rotated_buffers": n_tok,
+                "us": round(ms * 1e3, 2), "GB/s": gbs(byts, ms),
+                "bf16_input_us": round(ms_b * 1e3, 2), "bf16_input_GB/s": gbs(byts_b, ms_b),
+                "e8m0_us": round(ms_e * 1e3, 2), "e8m0_GB/s": gbs(byts_e, ms_e),
+                "per_block_rows": int(w.shape[0]), "per_block_rotated_buffers": n_blk,
+                "per_block_us": round(ms_w * 1e3, 2), "per_block_GB/s": gbs(byts_w, ms_w),
+                "per_block_e8m0_us": round(ms_we * 1e3, 2),
+                "per_block_e8m0_GB/s": gbs(byts_we, ms_we)})
+    return res
 
 
 def cpu_baseline(case, target_s: float):
@@ -293,7 +309,52 @@ def cpu_baseline(case, target_s: float):
     return {"value": round(flop / t / 1e12, 5), "unit": "TFLOPS", "cores": threads,
             "kind": "oracle",
             "sample": f"{len(sample)} of {len(routed)} routed rows of {case.name} "
-                      f"(all N={case.N} columns, K={K}), {t:.2f} s wall"}
+                      f"(all N={case.N} columns, K={K}), {t:.2f} s wall",
+            "cpu_model": cpu_model(),
+            "one_core": one_core_baselines()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def one_core_baselines(target_s: float = 3.0):
+    """The oracle on one thread: the whole 128 x 512 x 512 workload, and a
+    bounded sample of rows of 4096 x 7168 x 2048 (TFLOPS scaled to the
+    sample's own FLOP count)."""
+    import numpy as np
+    import oracle
+    from fp8_block_scaled_gemm_amd.inputs import workload
+
+    threads = oracle.num_threads()
+    out = {}
+    oracle.set_num_threads(1)
+    try:
+        for name in ("dense_128x512x512", "dense_4096x7168x2048"):
+            case = workload(name)
+            qa, sa = oracle.quantize_per_token(case.x_a.numpy())
+            qb, sb = oracle.quantize_per_block(case.x_b.numpy())
+            t0 = time.perf_counter()
+            oracle.gemm_nt(qa, sa, qb, sb, rows=np.arange(min(8, case.M)))
+            per_row = (time.perf_counter() - t0) / min(8, case.M)
+            n = int(min(case.M, max(8, target_s / max(per_row, 1e-9))))
+            rows = np.linspace(0, case.M - 1, n).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.gemm_nt(qa, sa, qb, sb, rows=rows)
+            t = time.perf_counter() - t0
+            out[name] = {"TFLOPS": round(2.0 * n * case.N * case.K / t / 1e12, 6),
+                         "rows": f"{n} of {case.M}", "s": round(t, 3)}
+    finally:
+        oracle.set_num_threads(threads)
+    return out
 
 
 def main():

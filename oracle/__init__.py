@@ -82,6 +82,8 @@ def _load():
     lib.orc_gemm_grouped_masked_rows.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -122,6 +124,11 @@ def bf16_from_double(v: float) -> int:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's later parallel loops (1 times one core)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- quantize

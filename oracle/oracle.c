@@ -485,3 +485,9 @@ int orc_num_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Set the thread count of later parallel regions (timing on one core). */
+void orc_set_num_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}

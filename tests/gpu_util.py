@@ -4,8 +4,8 @@ tolerance the workload fixes:
 
     |gpu - oracle| <= 2 * ulp_bf16(|oracle|) + 1e-3 * RMS(oracle)   per element
 
-with RMS over the call's routed elements, and bit-exact equality of every
-element the call must not write (they keep the 0xFFFF pre-fill)."""
+with RMS over every routed element of the call, and bit-exact equality of
+every element the call must not write (they keep the 0xFFFF pre-fill)."""
 from __future__ import annotations
 
 import numpy as np
@@ -58,3 +58,30 @@ def same_codes(a: np.ndarray, b: np.ndarray) -> bool:
     za = (a & 0x7F) == 0
     zb = (b & 0x7F) == 0
     return bool(np.array_equal(za, zb) and np.array_equal(a[~za], b[~zb]))
+
+
+def check_call(got_bits: np.ndarray, ref_bits: np.ndarray, routed: np.ndarray, what: str,
+               chunk_rows: int = 2048) -> float:
+    """Whole-call comparison of D viewed as [rows][N]: every row in ``routed``
+    against the oracle (RMS over all routed elements of the call, then the
+    per-element bound), every other row bit-exact at the 0xFFFF pre-fill.
+    Works in row chunks so full-size workloads stay within a few GB of host
+    memory."""
+    assert got_bits.shape == ref_bits.shape, (got_bits.shape, ref_bits.shape)
+    routed = np.asarray(routed, dtype=np.int64)
+    unrouted = np.ones(got_bits.shape[0], bool)
+    unrouted[routed] = False
+    assert (got_bits[unrouted] == 0xFFFF).all(), f"{what}: an unrouted row of D was written"
+    if routed.size == 0:
+        return 0.0
+    ss = 0.0
+    for c in range(0, routed.size, chunk_rows):
+        r = bf16_to_f64(ref_bits[routed[c:c + chunk_rows]])
+        assert np.isfinite(r).all(), f"{what}: oracle produced non-finite values"
+        ss += float(np.sum(r * r))
+    rms = float(np.sqrt(ss / (routed.size * got_bits.shape[1])))
+    worst = 0.0
+    for c in range(0, routed.size, chunk_rows):
+        rows = routed[c:c + chunk_rows]
+        worst = max(worst, assert_close_bf16(got_bits[rows], ref_bits[rows], what, rms=rms))
+    return worst

@@ -2,9 +2,10 @@
 
 Inputs are seeded fp32 draws quantized by the oracle's own quantizer (the GPU
 quantizer is checked separately, bit for bit), so no oracle input comes from
-the HIP path.  Small and medium cases compare every element; the full-size
-workloads compare sampled rows (the oracle computes them one by one) and
-check every unrouted row of D for the untouched 0xFFFF pre-fill."""
+the HIP path.  Every case, the full-size named workloads included, compares
+every routed element of D with the oracle's whole-call result (RMS taken over
+all routed elements of the call) and every unrouted row of D with its
+untouched 0xFFFF pre-fill."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +13,7 @@ import torch
 import fp8_block_scaled_gemm_amd as dg
 from fp8_block_scaled_gemm_amd.inputs import (contiguous_case, dense_case, masked_case,
                                               workload)
-from tests.gpu_util import SENTINEL, assert_close_bf16, to_dev
+from tests.gpu_util import SENTINEL, assert_close_bf16, check_call, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -79,11 +80,7 @@ def _check_full(orc, case):
     qa, sa, qb, sb = _prepared(orc, case)
     got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
     ref = _oracle_full(orc, case, qa, sa, qb, sb).reshape(-1, case.N)
-    rows = _routed_rows(case)
-    unrouted = np.setdiff1d(np.arange(got.shape[0]), rows)
-    assert (got[unrouted] == 0xFFFF).all(), "an unrouted row of D was written"
-    if rows.size:
-        assert_close_bf16(got[rows], ref[rows], case.name)
+    check_call(got, ref, _routed_rows(case), case.name)
     return got
 
 
@@ -301,24 +298,9 @@ FULL = ["dense_128x512x512", "dense_4096x7168x2048", "dense_64x7168x2048",
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(orc, name):
-    case = workload(name)
-    qa, sa, qb, sb = _prepared(orc, case)
-    got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
-    routed = _routed_rows(case)
-    unrouted = np.setdiff1d(np.arange(got.shape[0]), routed)
-    assert (got[unrouted] == 0xFFFF).all(), "an unrouted row of D was written"
-    rng = np.random.default_rng(len(name))
-    pick = np.unique(np.concatenate([routed[:2], routed[-2:],
-                                     rng.choice(routed, size=min(12, routed.size), replace=False)]))
-    if case.form == "dense":
-        ref = orc.gemm_nt(qa, sa, qb, sb, rows=pick)
-    elif case.form == "dense_acc":
-        ref = orc.gemm_nt_acc(qa[pick], sa[pick], qb, sb, case.x_c.numpy()[pick])
-    elif case.form == "contiguous":
-        ref = orc.gemm_grouped_contiguous(qa, sa, qb, sb, case.layout.numpy(), rows=pick)
-    else:
-        ref = orc.gemm_grouped_masked(qa, sa, qb, sb, case.masked_m.numpy(), rows=pick)
-    assert_close_bf16(got[pick], ref, name)
-    # no routed element may be left at the pre-fill
-    assert not (got[routed] == 0xFFFF).any()
+def test_full_size_every_routed_element(orc, name):
+    """The named workloads at their full sizes, in the launch configuration
+    the benchmark times: the oracle computes the whole call and every routed
+    element is compared."""
+    got = _check_full(orc, workload(name))
+    assert got.size
