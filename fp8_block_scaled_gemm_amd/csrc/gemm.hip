@@ -279,6 +279,84 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
     return true;
 }
 
+// Epilogue of a tile: the lane holds tile row 16 (WAVES_M i + wm) + lr and
+// columns wcol + 16j + 4lg .. +3 of acc[i][j].  DenseAcc adds the fp32 addend
+// C first; then the tile is rounded to bf16, staged in LDS (which every wave
+// must be done with) and stored row-predicated.
+template <class T, Form kForm>
+__device__ __forceinline__ void store_tile(v4f (&acc)[T::TM][T::TN], uint8_t* smem, int tid, int wm,
+                                           int wcol, int lr, int lg, const TileInfo& ti,
+                                           const float* __restrict__ C, uint16_t* __restrict__ D,
+                                           int64_t N) {
+    if constexpr (kForm == Form::DenseAcc) {
+        // D = bf16(C + acc): C is read straight into the accumulators'
+        // layout (one 16-byte load per sub-tile and lane), half of the
+        // wave's sub-tile rows at a time with all of that half's loads in
+        // flight, and added in fp32 before the single rounding below.  The
+        // buffer ends with the tile's last valid row: rows past it read as
+        // zero; columns past N of a valid row read C values of the next row
+        // (or zero after the last one) and are never stored.
+        const float* const tileC = C + ti.arow0 * N + ti.n0;
+        const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(tileC), (short)0,
+            (int)(uint32_t)(((int64_t)(ti.valid - 1) * N + (N - ti.n0)) * 4), 0x00020000);
+        constexpr int kH = T::TM / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4f c[kH][T::TN];
+#pragma unroll
+            for (int ii = 0; ii < kH; ++ii) {
+                const int row = 16 * (T::WAVES_M * (h * kH + ii) + wm) + lr;
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) {
+                    const uint32_t off = ((uint32_t)row * (uint32_t)N + wcol + 16 * j + 4 * lg) * 4u;
+                    c[ii][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < kH; ++ii)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) acc[h * kH + ii][j] += c[ii][j];
+        }
+    }
+    // Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage the whole tile
+    // in LDS, then write it back in full 16-byte chunks, consecutive lanes on
+    // consecutive chunks of a row.  In LDS (row pitch kPitchChunks chunks),
+    // 16-byte chunk c of row r sits at c ^ (r & 15): the 16 rows a fragment
+    // store touches land in distinct banks.
+    constexpr int kRowBytes = T::kPitchChunks * 16;
+    constexpr int kChunks = T::BN / 8;  // 16-byte chunks of an output row
+    uint8_t* const sD = smem;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+        const int row = 16 * (T::WAVES_M * i + wm) + lr;
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int col = wcol + 16 * j + 4 * lg;
+            const v2f lo = {acc[i][j][0], acc[i][j][1]};
+            const v2f hi = {acc[i][j][2], acc[i][j][3]};
+            v2u packed;
+            packed[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2bf));
+            packed[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2bf));
+            *reinterpret_cast<v2u*>(sD + row * kRowBytes + (((col >> 3) ^ (row & 15)) << 4) +
+                                    ((col >> 2) & 1) * 8) = packed;
+        }
+    }
+    __syncthreads();
+    static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
+#pragma unroll 4
+    for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
+        const int row = q / kChunks, c = q % kChunks;
+        const int64_t col = ti.n0 + c * 8;
+        bool ok = row < ti.valid && col < N;
+        if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
+        const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
+        // D is written once and not read back here: non-temporal stores keep
+        // it from evicting operand slabs that later tiles still read
+        if (ok) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col));
+    }
+}
+
 // Operands are separate __restrict__ arguments so the compiler knows they
 // are never written during the kernel.
 //
@@ -288,7 +366,7 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
 // time), passes the mid barrier, multiplies the rows [BM/2, BM), and passes
 // the end barrier.  Each wave loads its share of the slabs of block kb+2
 // straight from memory into LDS as soon as a barrier frees their buffer, so
-// every load has one and a half steps to land (see DG_STEP).
+// every load has one and a half steps to land (see `step`).
 //
 // Scales (kE8 = false): fp32, [rows][K/128] and [groups][NB][K/128], each K
 // block's partial promoted as acc += (sa sb) P.  With kE8: E8M0 exponent
@@ -329,23 +407,13 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
     // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
     // belongs at physical chunk l % 8 of row 8q + l / 8, i.e. chunk
-    // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  A slab's buffer starts at the K block
-    // in row 0 and ends with the tile's last valid row (A) or column (B), so
-    // rows past it read as zero; blocks past the last one get an empty
-    // buffer, so their loads move no data but still
-    // count towards the wave's vmcnt like every other step's.
+    // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  A slab's buffer starts at the
+    // K block in row 0 and ends with the tile's last valid row (A) or column
+    // (B), so rows past it read as zero; blocks past the last one get an
+    // empty buffer, so their loads move no data but still count towards the
+    // wave's vmcnt like every other step's.
     const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
     const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
-    // scale chunk loads: wave w < BM/64 fetches the four K blocks' row
-    // scales of rows [64w, 64w + 64) (16 bytes per row, or one 4-byte word
-    // of exponents), the next wave the column-block scales (fp32: lane l
-    // gets block l / 4, K block l % 4 of the chunk; E8M0: lane l gets the
-    // word of block l)
-    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)SP * (kE8 ? 1 : 4);
-    const uint32_t offSB = kE8 ? (uint32_t)lane * (uint32_t)SP
-                               : ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
-    constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
-    static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
     const int nb0 = ti.n0 >> 7;
     const int vn = (int)min<int64_t>(T::BN, N - ti.n0);
     // column-scale blocks the tile touches
@@ -354,50 +422,54 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     const ScaleT* tileSA = sa + ti.arow0 * SP;
     const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
     const ScaleT* tileSB = sb + ((int64_t)ti.g * NB + nb0) * SP;
-#define DG_ISSUE_A_PART(kb_, st_, i0_, i1_)                                                       \
-    do {                                                                                          \
-        const v4u rs_ = buffer_rsrc(tileA + (kb_) * 128,                                          \
-                                    (kb_) < KB ? (uint32_t)ti.valid * (uint32_t)K - (kb_) * 128 : 0u); \
-        _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i)                                     \
-            load_lds_16(rs_, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,                \
-                        smA + (st_) * T::kStageA + (wave + i * T::kWaves) * 1024);                \
-    } while (0)
-    // rows [0, BM/2) and [BM/2, BM) of the A slab
-#define DG_ISSUE_AL(kb_, st_) DG_ISSUE_A_PART(kb_, st_, 0, T::kLoadsA / 2)
-#define DG_ISSUE_AH(kb_, st_) DG_ISSUE_A_PART(kb_, st_, T::kLoadsA / 2, T::kLoadsA)
-#define DG_ISSUE_B(kb_, st_)                                                                      \
-    do {                                                                                          \
-        const v4u rs_ = buffer_rsrc(tileB + (kb_) * 128,                                          \
-                                    (kb_) < KB ? (uint32_t)vn * (uint32_t)K - (kb_) * 128 : 0u);  \
-        _Pragma("unroll") for (int i = 0; i < T::kLoadsB; ++i) {                                  \
-            if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;         \
-            load_lds_16(rs_, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,                \
-                        smB + (st_) * T::kStageB + (wave + i * T::kWaves) * 1024);                \
-        }                                                                                         \
-    } while (0)
+    // loads [i0, i1) of this wave's share of the A slab of block kb
+    auto issue_a = [&](int kb, int st, int i0, int i1) __attribute__((always_inline)) {
+        const v4u rs = buffer_rsrc(tileA + kb * 128,
+                                   kb < KB ? (uint32_t)ti.valid * (uint32_t)K - kb * 128 : 0u);
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+            load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
+                        smA + st * T::kStageA + (wave + i * T::kWaves) * 1024);
+    };
+    auto issue_b = [&](int kb, int st) __attribute__((always_inline)) {
+        const v4u rs = buffer_rsrc(tileB + kb * 128, kb < KB ? (uint32_t)vn * (uint32_t)K - kb * 128 : 0u);
+#pragma unroll
+        for (int i = 0; i < T::kLoadsB; ++i) {
+            if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;
+            load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
+                        smB + st * T::kStageB + (wave + i * T::kWaves) * 1024);
+        }
+    };
 
-    // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1.  The
-    // range check of a buffer load is per 4-byte word, so the words of a row's
-    // last chunk past K/128 (and rows past the valid ones) read as zero or as
-    // the next row's scales, which no step uses.  An exponent row's padding
-    // to 4 bytes keeps its chunk words aligned and in range.
-#define DG_ISSUE_SCALES(c_)                                                                       \
-    do {                                                                                          \
-        const int kb0_ = (c_) * 4;                                                                \
-        constexpr uint32_t kSz_ = sizeof(ScaleT);                                                 \
-        if (kb0_ < KB) {                                                                          \
-            if (wave < kScaleWaves) {                                                             \
-                const v4u rs_ = buffer_rsrc(tileSA + kb0_, (uint32_t)(ti.valid * SP - kb0_) * kSz_); \
-                if (kE8)                                                                          \
-                    load_lds_4(rs_, offSA, &smSA[(c_) & 1][wave * 64]);                           \
-                else                                                                              \
-                    load_lds_16(rs_, offSA, &smSA[(c_) & 1][wave * 64 * 4]);                      \
-            } else if (wave == kScaleWaves) {                                                     \
-                load_lds_4(buffer_rsrc(tileSB + kb0_, (uint32_t)(vnb * SP - kb0_) * kSz_),       \
-                           lane < (kE8 ? 1 : 4) * vnb ? offSB : 0xffffff00u, &smSB[(c_) & 1][0]); \
-            }                                                                                     \
-        }                                                                                         \
-    } while (0)
+    // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1: wave
+    // w < BM/64 fetches the four K blocks' row scales of rows [64w, 64w + 64)
+    // (16 bytes per row, or one 4-byte word of exponents), the next wave the
+    // column-block scales (fp32: lane l gets block l / 4, K block l % 4 of the
+    // chunk; E8M0: lane l gets the word of block l).  The range check of a
+    // buffer load is per 4-byte word, so the words of a row's last chunk past
+    // K/128 (and rows past the valid ones) read as zero or as the next row's
+    // scales, which no step uses.  An exponent row's padding to 4 bytes keeps
+    // its chunk words aligned and in range.
+    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)SP * (kE8 ? 1 : 4);
+    const uint32_t offSB = kE8 ? (uint32_t)lane * (uint32_t)SP
+                               : ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
+    constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
+    static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
+    auto issue_scales = [&](int c) __attribute__((always_inline)) {
+        const int kb0 = c * 4;
+        constexpr uint32_t kSz = sizeof(ScaleT);
+        if (kb0 >= KB) return;
+        if (wave < kScaleWaves) {
+            const v4u rs = buffer_rsrc(tileSA + kb0, (uint32_t)(ti.valid * SP - kb0) * kSz);
+            if (kE8)
+                load_lds_4(rs, offSA, &smSA[c & 1][wave * 64]);
+            else
+                load_lds_16(rs, offSA, &smSA[c & 1][wave * 64 * 4]);
+        } else if (wave == kScaleWaves) {
+            load_lds_4(buffer_rsrc(tileSB + kb0, (uint32_t)(vnb * SP - kb0) * kSz),
+                       lane < (kE8 ? 1 : 4) * vnb ? offSB : 0xffffff00u, &smSB[c & 1][0]);
+        }
+    };
 
     // ---- fragment reads.  Sub-tile row i of wave row wm covers tile rows
     // [16 (WAVES_M i + wm), +16): the wave rows interleave in 16-row steps, so
@@ -414,220 +486,127 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     int sblk[T::TN];
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) sblk[j] = (int)((ti.n0 + wcol + 16 * j) >> 7) - nb0;
-#define DG_FRAG(base_, off_)                                                                      \
-    join(*reinterpret_cast<const v4u*>((base_) + (off_) + chunk_lo),                             \
-         *reinterpret_cast<const v4u*>((base_) + (off_) + chunk_hi))
-#define DG_LOAD_BF(bf_, st_)                                                                      \
-    do {                                                                                          \
-        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                         \
-            bf_[j] = DG_FRAG(smB + (st_) * T::kStageB, fragB + j * 16 * 128);                     \
-    } while (0)
+    auto frag = [&](const uint8_t* p) __attribute__((always_inline)) {
+        return join(*reinterpret_cast<const v4u*>(p + chunk_lo), *reinterpret_cast<const v4u*>(p + chunk_hi));
+    };
 
     v4f acc[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    v8i bf[T::TN];
 
-    // sub-tile rows [i0_, i1_) of the wave tile for the K block on stage st_;
-    // with kSkipRows (a constexpr flag of the enclosing K loop copy, see
-    // below) rows that hold no valid row of the tile are skipped
-#define DG_ROWS(bf_use, kb_, st_, i0_, i1_)                                                       \
-    do {                                                                                          \
-        if constexpr (kE8) {                                                                      \
-            /* exponent chunks: one 4-byte word per row / column block */                        \
-            const uint8_t* eSA_ =                                                                 \
-                reinterpret_cast<const uint8_t*>(smSA[((kb_) >> 2) & 1]) + ((kb_) & 3);            \
-            const uint8_t* eSB_ =                                                                 \
-                reinterpret_cast<const uint8_t*>(smSB[((kb_) >> 2) & 1]) + ((kb_) & 3);            \
-            int e_b_[T::kOneScaleB ? 1 : T::TN];                                                  \
-            _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)               \
-                e_b_[j] = eSB_[sblk[j] * 4];                                                      \
-            _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                               \
-                if (kSkipRows && 16 * wm + kRowStep * i >= ti.valid) continue;       \
-                const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);   \
-                const int e_a_ = eSA_[(srow + kRowStep * i) * 4];                                 \
-                _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                 \
-                    acc[i][j] = mfma_block_e8(bf_use[j], af_, acc[i][j],                          \
-                                              e_b_[T::kOneScaleB ? 0 : j], e_a_);                 \
-            }                                                                                     \
-            break;                                                                                \
-        }                                                                                         \
-        const float* sSA_ = &smSA[((kb_) >> 2) & 1][(kb_) & 3];                                   \
-        const float* sSB_ = &smSB[((kb_) >> 2) & 1][(kb_) & 3];                                   \
-        float s_b_[T::kOneScaleB ? 1 : T::TN];                                                    \
-        _Pragma("unroll") for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j)                   \
-            s_b_[j] = sSB_[sblk[j] * 4];                                                          \
-        _Pragma("unroll") for (int i = (i0_); i < (i1_); ++i) {                                   \
-            if (kSkipRows && 16 * wm + kRowStep * i >= ti.valid) continue;           \
-            const v8i af_ = DG_FRAG(smA + (st_) * T::kStageA, fragA + i * kRowStep * 128);       \
-            const float s_a_ = sSA_[(srow + kRowStep * i) * 4];                                   \
-            _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                     \
-                acc[i][j] += (s_a_ * s_b_[T::kOneScaleB ? 0 : j]) * mfma_block(bf_use[j], af_);   \
-        }                                                                                         \
-    } while (0)
-    // one quarter of the wave tile's sub-tile rows
-#define DG_QUARTER(bf_use, kb_, st_, q_)                                                          \
-    DG_ROWS(bf_use, kb_, st_, (q_) * (T::TM / 4), ((q_) + 1) * (T::TM / 4))
+    // Sub-tile rows [i0, i1) of the wave tile for the K block kb on stage st.
+    // With kSkip, rows that hold no valid row of the tile are skipped.
+    auto mma_rows = [&](auto skip, int kb, int st, int i0, int i1) __attribute__((always_inline)) {
+        constexpr bool kSkip = decltype(skip)::value;
+        const uint8_t* stA = smA + st * T::kStageA + fragA;
+        if constexpr (kE8) {
+            // exponent chunks: one 4-byte word per row / column block
+            const uint8_t* eSA = reinterpret_cast<const uint8_t*>(smSA[(kb >> 2) & 1]) + (kb & 3);
+            const uint8_t* eSB = reinterpret_cast<const uint8_t*>(smSB[(kb >> 2) & 1]) + (kb & 3);
+            int e_b[T::kOneScaleB ? 1 : T::TN];
+#pragma unroll
+            for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) e_b[j] = eSB[sblk[j] * 4];
+#pragma unroll
+            for (int i = i0; i < i1; ++i) {
+                if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
+                const v8i af = frag(stA + i * kRowStep * 128);
+                const int e_a = eSA[(srow + kRowStep * i) * 4];
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = mfma_block_e8(bf[j], af, acc[i][j], e_b[T::kOneScaleB ? 0 : j], e_a);
+            }
+        } else {
+            const float* sSA = &smSA[(kb >> 2) & 1][kb & 3];
+            const float* sSB = &smSB[(kb >> 2) & 1][kb & 3];
+            float s_b[T::kOneScaleB ? 1 : T::TN];
+#pragma unroll
+            for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) s_b[j] = sSB[sblk[j] * 4];
+#pragma unroll
+            for (int i = i0; i < i1; ++i) {
+                if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
+                const v8i af = frag(stA + i * kRowStep * 128);
+                const float s_a = sSA[(srow + kRowStep * i) * 4];
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] += (s_a * s_b[T::kOneScaleB ? 0 : j]) * mfma_block(bf[j], af);
+            }
+        }
+    };
 
-    // One K block kb_ on stages st_ (= kb_ & 1), in two halves separated by
-    // a barrier.  The step starts by reading its B fragments (B slab of kb_);
-    // the first half multiplies the A rows [0, BM/2), the second half the rows
-    // [BM/2, BM).  A slab load is issued as soon as the barrier that frees its
-    // buffer has passed:
-    //   after the mid barrier: A rows [0, BM/2) and the B slab of block kb_+2
-    //     (their buffers held those of kb_);
-    //   after the end barrier: A rows [BM/2, BM) of block kb_+2.
-    // So every load has one and a half steps to land.  Loads of a wave
-    // complete in issue order; a barrier publishes what it needs by waiting
-    // until at most the loads issued after those (kAfter) remain.  Scale
-    // chunk loads (some waves, every fourth step) only make a wait stricter.
-#define DG_STEP(kb_, st_)                                                                         \
-    do {                                                                                          \
-        DG_LOAD_BF(bf, (st_));                                                                    \
-        DG_QUARTER(bf, kb_, st_, 0);                                                              \
-        DG_QUARTER(bf, kb_, st_, 1);                                                              \
-        wait_vmcnt_lgkm0<kAfter>(); /* A rows [BM/2, BM) of kb_ */                                \
-        lds_barrier();                                                                            \
-        DG_ISSUE_AL((kb_) + 2, (st_));                                                            \
-        DG_ISSUE_B((kb_) + 2, (st_));                                                             \
-        if (((kb_) & 3) == 0) DG_ISSUE_SCALES(((kb_) >> 2) + 1);                                  \
-        DG_QUARTER(bf, kb_, st_, 2);                                                              \
-        DG_QUARTER(bf, kb_, st_, 3);                                                              \
-        wait_vmcnt_lgkm0<kAfter>(); /* A rows [0, BM/2) and B of kb_+1 */                         \
-        lds_barrier();                                                                            \
-        DG_ISSUE_AH((kb_) + 2, (st_));                                                            \
-    } while (0)
-
-    // Loads a wave issues after the ones a barrier waits for (see above),
+    // Loads a wave issues after the ones a barrier waits for (see `step`),
     // counted for the wave that issues the fewest B loads.
     constexpr int kAfter = T::kLoadsA + T::kLoadsBMin;
     static_assert(T::kLoadsA % 2 == 0 && kAfter < 64, "A slab halves, vmcnt range");
 
-    v8i bf[T::TN];
+    // One K block kb on stage st (= kb & 1), in two halves separated by a
+    // barrier.  The step starts by reading its B fragments (B slab of kb);
+    // the first half multiplies the A rows [0, BM/2), the second half the rows
+    // [BM/2, BM).  A slab load is issued as soon as the barrier that frees its
+    // buffer has passed:
+    //   after the mid barrier: A rows [0, BM/2) and the B slab of block kb+2
+    //     (their buffers held those of kb);
+    //   after the end barrier: A rows [BM/2, BM) of block kb+2.
+    // So every load has one and a half steps to land.  Loads of a wave
+    // complete in issue order; a barrier publishes what it needs by waiting
+    // until at most the loads issued after those (kAfter) remain.  Scale
+    // chunk loads (some waves, every fourth step) only make a wait stricter.
+    auto step = [&](auto skip, int kb, int st) __attribute__((always_inline)) {
+        const uint8_t* stB = smB + st * T::kStageB + fragB;
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) bf[j] = frag(stB + j * 16 * 128);
+        mma_rows(skip, kb, st, 0, T::TM / 2);
+        wait_vmcnt_lgkm0<kAfter>();  // A rows [BM/2, BM) of kb
+        lds_barrier();
+        issue_a(kb + 2, st, 0, T::kLoadsA / 2);
+        issue_b(kb + 2, st);
+        if ((kb & 3) == 0) issue_scales((kb >> 2) + 1);
+        mma_rows(skip, kb, st, T::TM / 2, T::TM);
+        wait_vmcnt_lgkm0<kAfter>();  // A rows [0, BM/2) and B of kb+1
+        lds_barrier();
+        issue_a(kb + 2, st, T::kLoadsA / 2, T::kLoadsA);
+    };
+
     // Prologue: blocks 0 and 1 of A rows [0, BM/2) and of B, A rows
     // [BM/2, BM) of block 0 and scale chunk 0 land and are published; A rows
     // [BM/2, BM) of block 1 go last, as in the steady state, so that the
     // first waits count the same loads.
-    DG_ISSUE_SCALES(0);
-    DG_ISSUE_AL(0, 0);
-    DG_ISSUE_AH(0, 0);
-    DG_ISSUE_B(0, 0);
-    DG_ISSUE_AL(1, 1);
-    DG_ISSUE_B(1, 1);
+    issue_scales(0);
+    issue_a(0, 0, 0, T::kLoadsA);
+    issue_b(0, 0);
+    issue_a(1, 1, 0, T::kLoadsA / 2);
+    issue_b(1, 1);
     wait_vmcnt<0>();
     lds_barrier();
-    DG_ISSUE_AH(1, 1);
+    issue_a(1, 1, T::kLoadsA / 2, T::kLoadsA);
 
-#define DG_K_LOOP()                                                                               \
-    for (int kb = 0; kb < KB; kb += 2) {                                                          \
-        DG_STEP(kb, 0);                                                                           \
-        if (kb + 1 < KB) DG_STEP(kb + 1, 1);                                                      \
-    }
-    // A masked tile with rows past its group's count runs a copy of the loop
-    // that skips sub-tile rows without a valid row (kSkipRows).  With fp32
-    // scales full tiles keep the branch-free loop, whose schedule is faster;
-    // with E8M0 scales one skipping loop serves every tile (measured faster).
-    if constexpr (kForm == Form::Masked && kE8) {
-        constexpr bool kSkipRows = true;
-        DG_K_LOOP();
-    } else if constexpr (kForm == Form::Masked) {
-        if (ti.valid < T::BM) {
-            constexpr bool kSkipRows = true;
-            DG_K_LOOP();
-        } else {
-            constexpr bool kSkipRows = false;
-            DG_K_LOOP();
+    auto k_loop = [&](auto skip) __attribute__((always_inline)) {
+        for (int kb = 0; kb < KB; kb += 2) {
+            step(skip, kb, 0);
+            if (kb + 1 < KB) step(skip, kb + 1, 1);
         }
+    };
+    // A masked tile with rows past its group's count runs a copy of the loop
+    // that skips sub-tile rows without a valid row.  With fp32 scales full
+    // tiles keep the branch-free loop, whose schedule is faster; with E8M0
+    // scales one skipping loop serves every tile (measured faster).
+    if constexpr (kForm == Form::Masked && kE8) {
+        k_loop(std::true_type{});
+    } else if constexpr (kForm == Form::Masked) {
+        if (ti.valid < T::BM)
+            k_loop(std::true_type{});
+        else
+            k_loop(std::false_type{});
     } else {
-        constexpr bool kSkipRows = false;
-        DG_K_LOOP();
+        k_loop(std::false_type{});
     }
-#undef DG_K_LOOP
-#undef DG_STEP
-#undef DG_QUARTER
-#undef DG_ROWS
-#undef DG_LOAD_BF
-#undef DG_FRAG
-#undef DG_ISSUE_SCALES
-#undef DG_ISSUE_B
-#undef DG_ISSUE_AH
-#undef DG_ISSUE_AL
-#undef DG_ISSUE_A_PART
 
-    // ---- epilogue.  Lane holds tile row 16 (WAVES_M i + wm) + lr and
-    // columns wcol + 16j + 4lg .. +3.
+    // ---- epilogue
     wait_vmcnt<0>();  // the empty loads of the last steps have retired
     lds_barrier();
-    if constexpr (kForm == Form::DenseAcc) {
-        // D = bf16(C + acc): C is read straight into the accumulators'
-        // layout (one 16-byte load per sub-tile and lane), half of the
-        // wave's sub-tile rows at a time with all of that half's loads in
-        // flight, and added in fp32 before the single rounding below.  The
-        // buffer ends with the tile's last valid row: rows past it read as
-        // zero; columns past N of a valid row read C values of the next row
-        // (or zero after the last one) and are never stored.
-        const float* const tileC = C + ti.arow0 * N + ti.n0;
-        const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(tileC), (short)0,
-            (int)(uint32_t)(((int64_t)(ti.valid - 1) * N + (N - ti.n0)) * 4), 0x00020000);
-        constexpr int kH = T::TM / 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v4f c[kH][T::TN];
-#pragma unroll
-            for (int ii = 0; ii < kH; ++ii) {
-                const int row = 16 * (T::WAVES_M * (h * kH + ii) + wm) + lr;
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j) {
-                    const uint32_t off = ((uint32_t)row * (uint32_t)N + wcol + 16 * j + 4 * lg) * 4u;
-                    c[ii][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsC, off, 0, 0));
-                }
-            }
-#pragma unroll
-            for (int ii = 0; ii < kH; ++ii)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j) acc[h * kH + ii][j] += c[ii][j];
-        }
-    }
-    {
-        // Round to bf16 (v_cvt_pk_bf16_f32: nearest even), stage the whole
-        // tile in LDS, then write it back in full 16-byte chunks, consecutive
-        // lanes on consecutive chunks of a row.  In LDS (row pitch
-        // kPitchChunks chunks), 16-byte chunk c of row r sits at c ^ (r & 15):
-        // the 16 rows a fragment store touches land in distinct banks.
-        constexpr int kRowBytes = T::kPitchChunks * 16;
-        constexpr int kChunks = T::BN / 8;  // 16-byte chunks of an output row
-        uint8_t* const sD = smem;
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            const int row = 16 * (T::WAVES_M * i + wm) + lr;
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const int col = wcol + 16 * j + 4 * lg;
-                const v2f lo = {acc[i][j][0], acc[i][j][1]};
-                const v2f hi = {acc[i][j][2], acc[i][j][3]};
-                v2u packed;
-                packed[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2bf));
-                packed[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2bf));
-                *reinterpret_cast<v2u*>(sD + row * kRowBytes + (((col >> 3) ^ (row & 15)) << 4) +
-                                        ((col >> 2) & 1) * 8) = packed;
-            }
-        }
-        __syncthreads();
-        static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
-#pragma unroll 4
-        for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
-            const int row = q / kChunks, c = q % kChunks;
-            const int64_t col = ti.n0 + c * 8;
-            bool ok = row < ti.valid && col < N;
-            if (kForm == Form::Contiguous) ok = ok && (((row < 64 ? ti.ok0 : ti.ok1) >> (row & 63)) & 1);
-            const v4u v = *reinterpret_cast<const v4u*>(sD + row * kRowBytes + ((c ^ (row & 15)) << 4));
-            // D is written once and not read back here: non-temporal stores keep
-            // it from evicting operand slabs that later tiles still read
-            if (ok) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(D + (ti.arow0 + row) * N + col));
-        }
-    }
+    store_tile<T, kForm>(acc, smem, tid, wm, wcol, lr, lg, ti, C, D, N);
 }
 
 template <class T, Form kForm, bool kE8>
