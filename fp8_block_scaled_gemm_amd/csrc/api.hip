@@ -34,8 +34,6 @@ dg_status check_ptrs(const void* const* ptrs, int n) {
     return DG_OK;
 }
 
-dg_status from_hip(hipError_t e) { return e == hipSuccess ? DG_OK : DG_ERR_HIP; }
-
 // The three forms, with fp32 scales or (e8) E8M0 exponent bytes; the size
 // rules are the same for both.
 dg_status gemm_dense(const uint8_t* A, const void* sa, const uint8_t* B, const void* sb,
@@ -48,7 +46,7 @@ dg_status gemm_dense(const uint8_t* A, const void* sa, const uint8_t* B, const v
     if ((s = check_ptrs(ptrs, 5)) != DG_OK) return s;
     dg::GemmArgs a{A, sa, B, sb, D, nullptr, M, N, K, 1};
     a.e8m0 = e8;
-    return from_hip(dg::launch_gemm(dg::Form::Dense, a, static_cast<hipStream_t>(stream)));
+    return dg::launch_gemm(dg::Form::Dense, a, static_cast<hipStream_t>(stream));
 }
 
 dg_status gemm_contiguous(const uint8_t* A, const void* sa, const uint8_t* B, const void* sb,
@@ -64,7 +62,7 @@ dg_status gemm_contiguous(const uint8_t* A, const void* sa, const uint8_t* B, co
     if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
     dg::GemmArgs a{A, sa, B, sb, D, grouped_layout, M_sum, N, K, G};
     a.e8m0 = e8;
-    return from_hip(dg::launch_gemm(dg::Form::Contiguous, a, static_cast<hipStream_t>(stream)));
+    return dg::launch_gemm(dg::Form::Contiguous, a, static_cast<hipStream_t>(stream));
 }
 
 dg_status gemm_masked(const uint8_t* A, const void* sa, const uint8_t* B, const void* sb,
@@ -80,7 +78,7 @@ dg_status gemm_masked(const uint8_t* A, const void* sa, const uint8_t* B, const 
     if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
     dg::GemmArgs a{A, sa, B, sb, D, masked_m, M_max, N, K, G};
     a.e8m0 = e8;
-    return from_hip(dg::launch_gemm(dg::Form::Masked, a, static_cast<hipStream_t>(stream)));
+    return dg::launch_gemm(dg::Form::Masked, a, static_cast<hipStream_t>(stream));
 }
 
 dg_status check_quantize(const void* x, int64_t rows, int64_t K, const void* q, const void* s,
@@ -118,7 +116,7 @@ dg_status dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sa, const uint8_t* B
     const void* ptrs[] = {A, sa, B, sb, C, D};
     if ((s = check_ptrs(ptrs, 6)) != DG_OK) return s;
     dg::GemmArgs a{A, sa, B, sb, D, nullptr, M, N, K, 1, C};
-    return from_hip(dg::launch_gemm(dg::Form::DenseAcc, a, static_cast<hipStream_t>(stream)));
+    return dg::launch_gemm(dg::Form::DenseAcc, a, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_fp8_gemm_grouped_contiguous(const uint8_t* A, const float* sa, const uint8_t* B,
@@ -153,38 +151,35 @@ dg_status dg_quantize_fp8_per_token(const float* x, int64_t M, int64_t K, uint8_
                                     void* stream) {
     const dg_status st = check_quantize(x, M, K, q, s, false);
     if (st != DG_OK || M == 0) return st;
-    return from_hip(dg::launch_quantize_per_token(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+    return dg::launch_quantize_per_token(x, M, K, q, s, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_quantize_fp8_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                                          float* s, void* stream) {
     const dg_status st = check_quantize(x, M, K, q, s, false);
     if (st != DG_OK || M == 0) return st;
-    return from_hip(
-        dg::launch_quantize_per_token_bf16(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+    return dg::launch_quantize_per_token_bf16(x, M, K, q, s, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_quantize_fp8_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
                                     void* stream) {
     const dg_status st = check_quantize(x, N, K, q, s, true);
     if (st != DG_OK || N == 0) return st;
-    return from_hip(dg::launch_quantize_per_block(x, N, K, q, s, static_cast<hipStream_t>(stream)));
+    return dg::launch_quantize_per_block(x, N, K, q, s, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_quantize_fp8_per_token_e8m0(const float* x, int64_t M, int64_t K, uint8_t* q,
                                          uint8_t* s, void* stream) {
     const dg_status st = check_quantize(x, M, K, q, s, false);
     if (st != DG_OK || M == 0) return st;
-    return from_hip(
-        dg::launch_quantize_per_token_e8m0(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+    return dg::launch_quantize_per_token_e8m0(x, M, K, q, s, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_quantize_fp8_per_block_e8m0(const float* x, int64_t N, int64_t K, uint8_t* q,
                                          uint8_t* s, void* stream) {
     const dg_status st = check_quantize(x, N, K, q, s, true);
     if (st != DG_OK || N == 0) return st;
-    return from_hip(
-        dg::launch_quantize_per_block_e8m0(x, N, K, q, s, static_cast<hipStream_t>(stream)));
+    return dg::launch_quantize_per_block_e8m0(x, N, K, q, s, static_cast<hipStream_t>(stream));
 }
 
 const char* dg_status_string(dg_status status) {

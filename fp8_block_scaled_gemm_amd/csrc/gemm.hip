@@ -610,7 +610,7 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
 }
 
 template <class T, Form kForm, bool kE8>
-static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
+static dg_status launch_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t m_blocks = (a.rows + T::BM - 1) / T::BM;
     const int64_t n_blocks = (a.N + T::BN - 1) / T::BN;
     int64_t grid;
@@ -620,17 +620,17 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
     } else {
         grid = (m_blocks * n_blocks + kNumXcds - 1) / kNumXcds * kNumXcds;
     }
-    if (grid == 0) return hipSuccess;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (grid == 0) return DG_OK;
+    if (grid > 0x7fffffff) return DG_ERR_SHAPE;
     // per-lane 32-bit offsets: a tile's rows of K bytes, its A scales
-    if ((int64_t)std::max(T::BM, T::BN) * a.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    if ((int64_t)std::max(T::BM, T::BN) * a.K >= (int64_t(1) << 32)) return DG_ERR_SHAPE;
     // and a tile's rows of fp32 C
     if (kForm == Form::DenseAcc && (int64_t)T::BM * a.N * 4 >= (int64_t(1) << 32))
-        return hipErrorInvalidValue;
+        return DG_ERR_SHAPE;
     hipLaunchKernelGGL((gemm_kernel<T, kForm, kE8>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
                        a.A, a.sa, a.B, a.sb, a.D, a.aux, a.C, a.rows, a.N, a.K, a.G, (int)m_blocks,
                        (int)n_blocks);
-    return hipGetLastError();
+    return launched();
 }
 
 // 256x256 tiles, 8 waves of 128x64 (two per SIMD).
@@ -703,7 +703,7 @@ static int forced_dense_shape() {
 // K = 2048), and 128x32 tiles put the most B loads in flight (measured on
 // 128 x 7168 x 2048: 13.7 us against 17.7 with 128x128 and 24 with 128x256).
 template <Form kForm, bool kE8>
-static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
+static dg_status launch_dense(const GemmArgs& a, hipStream_t stream) {
     struct Shape { int bm, bn; double rel; int id; };
     // per-area costs from measured loop cycles per K block (256x256: 3.43k,
     // 256x224: 3.42k, 256x192: 2.93k, 128x256: 2.08k cycles); 256x160 from
@@ -744,13 +744,13 @@ static hipError_t launch_dense(const GemmArgs& a, hipStream_t stream) {
     }
 }
 
-hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
+dg_status launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
     if (a.e8m0) {
         switch (form) {
             case Form::Dense: return launch_dense<Form::Dense, true>(a, stream);
             case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous, true>(a, stream);
             case Form::Masked: return launch_tiled<TileLargeT, Form::Masked, true>(a, stream);
-            default: return hipErrorInvalidValue;
+            default: return DG_ERR_UNSUPPORTED;
         }
     }
     switch (form) {
@@ -759,7 +759,7 @@ hipError_t launch_gemm(Form form, const GemmArgs& a, hipStream_t stream) {
         case Form::Contiguous: return launch_tiled<TileRows128, Form::Contiguous, false>(a, stream);
         case Form::Masked: return launch_tiled<TileMasked, Form::Masked, false>(a, stream);
     }
-    return hipErrorInvalidValue;
+    return DG_ERR_UNSUPPORTED;
 }
 
 }  // namespace dg

@@ -184,47 +184,47 @@ __global__ __launch_bounds__(256) void quantize_per_block_kernel(
 }
 
 template <class In, bool kE8>
-static hipError_t launch_per_token(const In* x, int64_t M, int64_t K, uint8_t* q, void* s,
+static dg_status launch_per_token(const In* x, int64_t M, int64_t K, uint8_t* q, void* s,
                                    hipStream_t stream) {
     const int64_t total = M * (K >> 7);
     const int64_t grid = (total + 31) / 32;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (grid > 0x7fffffff) return DG_ERR_SHAPE;
     hipLaunchKernelGGL((quantize_per_token_kernel<In, kE8>), dim3((unsigned)grid), dim3(256), 0,
                        stream, x, total, K, q, s);
-    return hipGetLastError();
+    return launched();
 }
 
 template <bool kE8>
-static hipError_t launch_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, void* s,
+static dg_status launch_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, void* s,
                                    hipStream_t stream) {
     const int64_t NB = (N + 127) / 128, KB = K >> 7;
-    if (NB > 65535 || KB > 0x7fffffff) return hipErrorInvalidValue;
+    if (NB > 65535 || KB > 0x7fffffff) return DG_ERR_SHAPE;
     hipLaunchKernelGGL(quantize_per_block_kernel<kE8>, dim3((unsigned)KB, (unsigned)NB), dim3(256),
                        0, stream, x, N, K, q, s);
-    return hipGetLastError();
+    return launched();
 }
 
-hipError_t launch_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
+dg_status launch_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream) {
     return launch_per_token<float, false>(x, M, K, q, s, stream);
 }
 
-hipError_t launch_quantize_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+dg_status launch_quantize_per_token_bf16(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                                           float* s, hipStream_t stream) {
     return launch_per_token<uint16_t, false>(x, M, K, q, s, stream);
 }
 
-hipError_t launch_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
+dg_status launch_quantize_per_block(const float* x, int64_t N, int64_t K, uint8_t* q, float* s,
                                      hipStream_t stream) {
     return launch_per_block<false>(x, N, K, q, s, stream);
 }
 
-hipError_t launch_quantize_per_token_e8m0(const float* x, int64_t M, int64_t K, uint8_t* q,
+dg_status launch_quantize_per_token_e8m0(const float* x, int64_t M, int64_t K, uint8_t* q,
                                           uint8_t* s, hipStream_t stream) {
     return launch_per_token<float, true>(x, M, K, q, s, stream);
 }
 
-hipError_t launch_quantize_per_block_e8m0(const float* x, int64_t N, int64_t K, uint8_t* q,
+dg_status launch_quantize_per_block_e8m0(const float* x, int64_t N, int64_t K, uint8_t* q,
                                           uint8_t* s, hipStream_t stream) {
     return launch_per_block<true>(x, N, K, q, s, stream);
 }

@@ -33,6 +33,8 @@
  *   - Rows that a call does not route (M tail, padding rows of the
  *     contiguous form, rows past masked_m in the masked form) are never
  *     written.
+ *   - Sizes that pass a call's rules but would need a grid of more than
+ *     2^31 - 1 workgroups return DG_ERR_SHAPE, with nothing enqueued.
  *   - A launch failure reported by the HIP runtime returns DG_ERR_HIP.
  *   - Calls on different streams may run concurrently; they share nothing.
  */

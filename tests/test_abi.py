@@ -178,3 +178,16 @@ def test_binding_refuses_tensors_on_two_devices():
     assert dg._device_of(a, a) == a.device
     with pytest.raises(ValueError, match="one device"):
         dg._device_of(a, b)
+
+
+def test_launch_limits_are_shape_errors(lib):
+    """Sizes that pass the per-call rules but would need more than 2^31
+    workgroups are rejected as DG_ERR_SHAPE before anything is enqueued."""
+    g = lib.dg_fp8_gemm_grouped_masked
+    # 2^20 slabs of one 256-row block times 4096 column blocks: 2^32 tiles
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 256, 1 << 20, 128, None) == DG_ERR_SHAPE
+    # 2^37 (row, K block) pairs over 32 per workgroup: 2^32 workgroups
+    assert lib.dg_quantize_fp8_per_token(FAKE, 1 << 30, 1 << 14, FAKE, FAKE, None) == DG_ERR_SHAPE
+    assert lib.dg_quantize_fp8_per_token_e8m0(FAKE, 1 << 30, 1 << 14, FAKE, FAKE, None) == DG_ERR_SHAPE
+    # dense: 2^23 x 2^12 tiles of 256 x 256
+    assert _gemm_nt(lib, M=(1 << 31) - 1, N=1 << 20) == DG_ERR_SHAPE
