@@ -228,11 +228,29 @@ __device__ __forceinline__ bool masked_slot(int b, int m_blocks, int n_blocks, i
     return false;
 }
 
+// Contiguous form: the largest valid group id below `below` among the rows
+// of the 128-row block at ti.m0 and the masks of the rows carrying it; false
+// when there is none.  Every wave computes this from the layout itself.
+__device__ __forceinline__ bool block_group(const int32_t* __restrict__ layout, int64_t G, int below,
+                                            int lane, TileInfo& ti) {
+    const int id0 = layout[ti.m0 + lane], id1 = layout[ti.m0 + 64 + lane];
+    auto usable = [&](int id) { return id >= 0 && id < G && id < below; };
+    int gid = max(usable(id0) ? id0 : -1, usable(id1) ? id1 : -1);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) gid = max(gid, __shfl_xor(gid, d, 64));
+    gid = __builtin_amdgcn_readfirstlane(gid);
+    if (gid < 0) return false;
+    ti.g = gid;
+    ti.ok0 = __ballot(id0 == gid);
+    ti.ok1 = __ballot(id1 == gid);
+    return true;
+}
+
 // Decode workgroup `b`'s tile; false when it is a padding slot or the tile
 // has no routed row (masked rows past masked_m, contiguous blocks of
-// padding).  Contiguous: the block's group is the largest id in [0, G) among
-// its rows (the layout puts one id per 128-row block), and only rows carrying
-// that id are routed; every wave computes this from the layout itself.
+// padding).  Contiguous: the block's first group is the largest id in
+// [0, G) among its rows (the layout puts one id per 128-row block); a block
+// that mixes ids is then run again for each smaller id (see gemm_kernel).
 template <class T, Form kForm>
 __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, int64_t rows,
                                             int64_t G, const int32_t* __restrict__ aux,
@@ -264,15 +282,7 @@ __device__ __forceinline__ bool decode_tile(int b, int m_blocks, int n_blocks, i
         ti.arow0 = ti.m0;
     } else {
         static_assert(kForm != Form::Contiguous || T::BM == 128, "one group per 128-row block");
-        const int id0 = aux[ti.m0 + lane], id1 = aux[ti.m0 + 64 + lane];
-        int gid = max((id0 >= 0 && id0 < G) ? id0 : -1, (id1 >= 0 && id1 < G) ? id1 : -1);
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) gid = max(gid, __shfl_xor(gid, d, 64));
-        gid = __builtin_amdgcn_readfirstlane(gid);
-        if (gid < 0) return false;
-        ti.g = gid;
-        ti.ok0 = __ballot(id0 == gid);
-        ti.ok1 = __ballot(id1 == gid);
+        if (!block_group(aux, G, (int)G, lane, ti)) return false;
         ti.valid = T::BM;
         ti.arow0 = ti.m0;
     }
@@ -372,7 +382,7 @@ __device__ __forceinline__ void store_tile(v4f (&acc)[T::TM][T::TN], uint8_t* sm
 // block's partial promoted as acc += (sa sb) P.  With kE8: E8M0 exponent
 // bytes, rows padded to a multiple of 4 bytes ([rows][SP], [groups][NB][SP]),
 // applied by the scaled MFMA itself, which accumulates straight into acc.
-template <class T, Form kForm, bool kE8>
+template <class T, Form kForm, bool kE8, bool kMixed = false>
 __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     const uint8_t* __restrict__ A, const void* __restrict__ sa_v, const uint8_t* __restrict__ B,
     const void* __restrict__ sb_v, uint16_t* __restrict__ D, const int32_t* __restrict__ aux,
@@ -399,214 +409,241 @@ __global__ __launch_bounds__(T::kThreads, 2) void gemm_kernel(
     const int wcol = wn * T::WN;
 
     TileInfo ti;
-    if (!decode_tile<T, kForm>(blockIdx.x, m_blocks, n_blocks, rows, G, aux, lane, ti)) return;
-
-    uint8_t* const smA = smem;
-    uint8_t* const smB = smem + 2 * T::kStageA;
-
-    // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
-    // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
-    // belongs at physical chunk l % 8 of row 8q + l / 8, i.e. chunk
-    // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  A slab's buffer starts at the
-    // K block in row 0 and ends with the tile's last valid row (A) or column
-    // (B), so rows past it read as zero; blocks past the last one get an
-    // empty buffer, so their loads move no data but still count towards the
-    // wave's vmcnt like every other step's.
-    const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
-    const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
-    const int nb0 = ti.n0 >> 7;
-    const int vn = (int)min<int64_t>(T::BN, N - ti.n0);
-    // column-scale blocks the tile touches
-    const int vnb = (int)((ti.n0 + vn - 1) >> 7) - nb0 + 1;
-    const uint8_t* tileA = A + ti.arow0 * K;
-    const ScaleT* tileSA = sa + ti.arow0 * SP;
-    const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
-    const ScaleT* tileSB = sb + ((int64_t)ti.g * NB + nb0) * SP;
-    // loads [i0, i1) of this wave's share of the A slab of block kb
-    auto issue_a = [&](int kb, int st, int i0, int i1) __attribute__((always_inline)) {
-        const v4u rs = buffer_rsrc(tileA + kb * 128,
-                                   kb < KB ? (uint32_t)ti.valid * (uint32_t)K - kb * 128 : 0u);
-#pragma unroll
-        for (int i = i0; i < i1; ++i)
-            load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
-                        smA + st * T::kStageA + (wave + i * T::kWaves) * 1024);
-    };
-    auto issue_b = [&](int kb, int st) __attribute__((always_inline)) {
-        const v4u rs = buffer_rsrc(tileB + kb * 128, kb < KB ? (uint32_t)vn * (uint32_t)K - kb * 128 : 0u);
-#pragma unroll
-        for (int i = 0; i < T::kLoadsB; ++i) {
-            if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;
-            load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
-                        smB + st * T::kStageB + (wave + i * T::kWaves) * 1024);
-        }
-    };
-
-    // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1: wave
-    // w < BM/64 fetches the four K blocks' row scales of rows [64w, 64w + 64)
-    // (16 bytes per row, or one 4-byte word of exponents), the next wave the
-    // column-block scales (fp32: lane l gets block l / 4, K block l % 4 of the
-    // chunk; E8M0: lane l gets the word of block l).  The range check of a
-    // buffer load is per 4-byte word, so the words of a row's last chunk past
-    // K/128 (and rows past the valid ones) read as zero or as the next row's
-    // scales, which no step uses.  An exponent row's padding to 4 bytes keeps
-    // its chunk words aligned and in range.
-    const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)SP * (kE8 ? 1 : 4);
-    const uint32_t offSB = kE8 ? (uint32_t)lane * (uint32_t)SP
-                               : ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
-    constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
-    static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
-    auto issue_scales = [&](int c) __attribute__((always_inline)) {
-        const int kb0 = c * 4;
-        constexpr uint32_t kSz = sizeof(ScaleT);
-        if (kb0 >= KB) return;
-        if (wave < kScaleWaves) {
-            const v4u rs = buffer_rsrc(tileSA + kb0, (uint32_t)(ti.valid * SP - kb0) * kSz);
-            if (kE8)
-                load_lds_4(rs, offSA, &smSA[c & 1][wave * 64]);
-            else
-                load_lds_16(rs, offSA, &smSA[c & 1][wave * 64 * 4]);
-        } else if (wave == kScaleWaves) {
-            load_lds_4(buffer_rsrc(tileSB + kb0, (uint32_t)(vnb * SP - kb0) * kSz),
-                       lane < (kE8 ? 1 : 4) * vnb ? offSB : 0xffffff00u, &smSB[c & 1][0]);
-        }
-    };
-
-    // ---- fragment reads.  Sub-tile row i of wave row wm covers tile rows
-    // [16 (WAVES_M i + wm), +16): the wave rows interleave in 16-row steps, so
-    // a partial tile (a masked group's last rows, a ragged M) leaves work on
-    // every wave.  Every row r a lane reads is lr plus a multiple of 16, so
-    // r & 7 == lr & 7 and the swizzled chunk offsets are per-lane constants;
-    // sub-tile i (or j) only adds a multiple of 16 rows (an immediate).
-    static_assert(T::WN % 16 == 0, "wave column offsets keep the row swizzle");
-    constexpr int kRowStep = 16 * T::WAVES_M;
-    const int chunk_lo = (lg ^ (lr & 7)) << 4, chunk_hi = ((lg + 4) ^ (lr & 7)) << 4;
-    const int fragA = (16 * wm + lr) * 128, fragB = (wcol + lr) * 128;
-    const int srow = 16 * wm + lr;
-    // column-scale block of sub-tile j, relative to the tile's first one
-    int sblk[T::TN];
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j) sblk[j] = (int)((ti.n0 + wcol + 16 * j) >> 7) - nb0;
-    auto frag = [&](const uint8_t* p) __attribute__((always_inline)) {
-        return join(*reinterpret_cast<const v4u*>(p + chunk_lo), *reinterpret_cast<const v4u*>(p + chunk_hi));
-    };
-
-    v4f acc[T::TM][T::TN];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    v8i bf[T::TN];
-
-    // Sub-tile rows [i0, i1) of the wave tile for the K block kb on stage st.
-    // With kSkip, rows that hold no valid row of the tile are skipped.
-    auto mma_rows = [&](auto skip, int kb, int st, int i0, int i1) __attribute__((always_inline)) {
-        constexpr bool kSkip = decltype(skip)::value;
-        const uint8_t* stA = smA + st * T::kStageA + fragA;
-        if constexpr (kE8) {
-            // exponent chunks: one 4-byte word per row / column block
-            const uint8_t* eSA = reinterpret_cast<const uint8_t*>(smSA[(kb >> 2) & 1]) + (kb & 3);
-            const uint8_t* eSB = reinterpret_cast<const uint8_t*>(smSB[(kb >> 2) & 1]) + (kb & 3);
-            int e_b[T::kOneScaleB ? 1 : T::TN];
-#pragma unroll
-            for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) e_b[j] = eSB[sblk[j] * 4];
-#pragma unroll
-            for (int i = i0; i < i1; ++i) {
-                if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
-                const v8i af = frag(stA + i * kRowStep * 128);
-                const int e_a = eSA[(srow + kRowStep * i) * 4];
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = mfma_block_e8(bf[j], af, acc[i][j], e_b[T::kOneScaleB ? 0 : j], e_a);
-            }
-        } else {
-            const float* sSA = &smSA[(kb >> 2) & 1][kb & 3];
-            const float* sSB = &smSB[(kb >> 2) & 1][kb & 3];
-            float s_b[T::kOneScaleB ? 1 : T::TN];
-#pragma unroll
-            for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) s_b[j] = sSB[sblk[j] * 4];
-#pragma unroll
-            for (int i = i0; i < i1; ++i) {
-                if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
-                const v8i af = frag(stA + i * kRowStep * 128);
-                const float s_a = sSA[(srow + kRowStep * i) * 4];
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] += (s_a * s_b[T::kOneScaleB ? 0 : j]) * mfma_block(bf[j], af);
-            }
-        }
-    };
-
-    // Loads a wave issues after the ones a barrier waits for (see `step`),
-    // counted for the wave that issues the fewest B loads.
-    constexpr int kAfter = T::kLoadsA + T::kLoadsBMin;
-    static_assert(T::kLoadsA % 2 == 0 && kAfter < 64, "A slab halves, vmcnt range");
-
-    // One K block kb on stage st (= kb & 1), in two halves separated by a
-    // barrier.  The step starts by reading its B fragments (B slab of kb);
-    // the first half multiplies the A rows [0, BM/2), the second half the rows
-    // [BM/2, BM).  A slab load is issued as soon as the barrier that frees its
-    // buffer has passed:
-    //   after the mid barrier: A rows [0, BM/2) and the B slab of block kb+2
-    //     (their buffers held those of kb);
-    //   after the end barrier: A rows [BM/2, BM) of block kb+2.
-    // So every load has one and a half steps to land.  Loads of a wave
-    // complete in issue order; a barrier publishes what it needs by waiting
-    // until at most the loads issued after those (kAfter) remain.  Scale
-    // chunk loads (some waves, every fourth step) only make a wait stricter.
-    auto step = [&](auto skip, int kb, int st) __attribute__((always_inline)) {
-        const uint8_t* stB = smB + st * T::kStageB + fragB;
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) bf[j] = frag(stB + j * 16 * 128);
-        mma_rows(skip, kb, st, 0, T::TM / 2);
-        wait_vmcnt_lgkm0<kAfter>();  // A rows [BM/2, BM) of kb
-        lds_barrier();
-        issue_a(kb + 2, st, 0, T::kLoadsA / 2);
-        issue_b(kb + 2, st);
-        if ((kb & 3) == 0) issue_scales((kb >> 2) + 1);
-        mma_rows(skip, kb, st, T::TM / 2, T::TM);
-        wait_vmcnt_lgkm0<kAfter>();  // A rows [0, BM/2) and B of kb+1
-        lds_barrier();
-        issue_a(kb + 2, st, T::kLoadsA / 2, T::kLoadsA);
-    };
-
-    // Prologue: blocks 0 and 1 of A rows [0, BM/2) and of B, A rows
-    // [BM/2, BM) of block 0 and scale chunk 0 land and are published; A rows
-    // [BM/2, BM) of block 1 go last, as in the steady state, so that the
-    // first waits count the same loads.
-    issue_scales(0);
-    issue_a(0, 0, 0, T::kLoadsA);
-    issue_b(0, 0);
-    issue_a(1, 1, 0, T::kLoadsA / 2);
-    issue_b(1, 1);
-    wait_vmcnt<0>();
-    lds_barrier();
-    issue_a(1, 1, T::kLoadsA / 2, T::kLoadsA);
-
-    auto k_loop = [&](auto skip) __attribute__((always_inline)) {
-        for (int kb = 0; kb < KB; kb += 2) {
-            step(skip, kb, 0);
-            if (kb + 1 < KB) step(skip, kb + 1, 1);
-        }
-    };
-    // A masked tile with rows past its group's count runs a copy of the loop
-    // that skips sub-tile rows without a valid row.  With fp32 scales full
-    // tiles keep the branch-free loop, whose schedule is faster; with E8M0
-    // scales one skipping loop serves every tile (measured faster).
-    if constexpr (kForm == Form::Masked && kE8) {
-        k_loop(std::true_type{});
-    } else if constexpr (kForm == Form::Masked) {
-        if (ti.valid < T::BM)
-            k_loop(std::true_type{});
-        else
-            k_loop(std::false_type{});
+    if constexpr (kMixed) {
+        // the 128-row block blockIdx.x, from its second largest valid id on
+        // (the largest one's rows are the ordinary launch's), column tile 0
+        static_assert(kForm == Form::Contiguous, "mixed blocks are a contiguous-form case");
+        ti.m0 = blockIdx.x * T::BM;
+        ti.n0 = 0;
+        ti.valid = T::BM;
+        ti.arow0 = ti.m0;
+        if (!block_group(aux, G, (int)G, lane, ti) || !block_group(aux, G, ti.g, lane, ti)) return;
     } else {
-        k_loop(std::false_type{});
+        if (!decode_tile<T, kForm>(blockIdx.x, m_blocks, n_blocks, rows, G, aux, lane, ti)) return;
     }
 
-    // ---- epilogue
-    wait_vmcnt<0>();  // the empty loads of the last steps have retired
-    lds_barrier();
-    store_tile<T, kForm>(acc, smem, tid, wm, wcol, lr, lg, ti, C, D, N);
+    // One pass per tile; the mixed-block launch walks every column tile of
+    // its block for each of its smaller ids, each pass storing only the rows
+    // of its own id.
+    for (;;) {
+        uint8_t* const smA = smem;
+        uint8_t* const smB = smem + 2 * T::kStageA;
+
+        // ---- slab loads.  A wave's load i fills rows [8q, 8q+8) of a stage,
+        // q = wave + i * kWaves; lane l fetches the logical 16-byte chunk that
+        // belongs at physical chunk l % 8 of row 8q + l / 8, i.e. chunk
+        // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  A slab's buffer starts at the
+        // K block in row 0 and ends with the tile's last valid row (A) or column
+        // (B), so rows past it read as zero; blocks past the last one get an
+        // empty buffer, so their loads move no data but still count towards the
+        // wave's vmcnt like every other step's.
+        const int sub = lane >> 3, lchunk = (lane & 7) ^ sub;
+        const uint32_t offRow = (uint32_t)(wave * 8 + sub) * (uint32_t)K + lchunk * 16;
+        const int nb0 = ti.n0 >> 7;
+        const int vn = (int)min<int64_t>(T::BN, N - ti.n0);
+        // column-scale blocks the tile touches
+        const int vnb = (int)((ti.n0 + vn - 1) >> 7) - nb0 + 1;
+        const uint8_t* tileA = A + ti.arow0 * K;
+        const ScaleT* tileSA = sa + ti.arow0 * SP;
+        const uint8_t* tileB = B + ((int64_t)ti.g * N + ti.n0) * K;
+        const ScaleT* tileSB = sb + ((int64_t)ti.g * NB + nb0) * SP;
+        // loads [i0, i1) of this wave's share of the A slab of block kb
+        auto issue_a = [&](int kb, int st, int i0, int i1) __attribute__((always_inline)) {
+            const v4u rs = buffer_rsrc(tileA + kb * 128,
+                                       kb < KB ? (uint32_t)ti.valid * (uint32_t)K - kb * 128 : 0u);
+#pragma unroll
+            for (int i = i0; i < i1; ++i)
+                load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
+                            smA + st * T::kStageA + (wave + i * T::kWaves) * 1024);
+        };
+        auto issue_b = [&](int kb, int st) __attribute__((always_inline)) {
+            const v4u rs = buffer_rsrc(tileB + kb * 128, kb < KB ? (uint32_t)vn * (uint32_t)K - kb * 128 : 0u);
+#pragma unroll
+            for (int i = 0; i < T::kLoadsB; ++i) {
+                if ((T::BN / 8) % T::kWaves != 0 && wave + i * T::kWaves >= T::BN / 8) break;
+                load_lds_16(rs, offRow + (uint32_t)(i * T::kWaves * 8) * (uint32_t)K,
+                            smB + st * T::kStageB + (wave + i * T::kWaves) * 1024);
+            }
+        };
+
+        // Scale chunk c (K blocks 4c .. 4c+3) into chunk buffer c & 1: wave
+        // w < BM/64 fetches the four K blocks' row scales of rows [64w, 64w + 64)
+        // (16 bytes per row, or one 4-byte word of exponents), the next wave the
+        // column-block scales (fp32: lane l gets block l / 4, K block l % 4 of the
+        // chunk; E8M0: lane l gets the word of block l).  The range check of a
+        // buffer load is per 4-byte word, so the words of a row's last chunk past
+        // K/128 (and rows past the valid ones) read as zero or as the next row's
+        // scales, which no step uses.  An exponent row's padding to 4 bytes keeps
+        // its chunk words aligned and in range.
+        const uint32_t offSA = (uint32_t)(wave * 64 + lane) * (uint32_t)SP * (kE8 ? 1 : 4);
+        const uint32_t offSB = kE8 ? (uint32_t)lane * (uint32_t)SP
+                                   : ((uint32_t)(lane >> 2) * (uint32_t)KB + (lane & 3)) * 4;
+        constexpr int kScaleWaves = T::BM / 64;  // waves that fetch row scales
+        static_assert(kScaleWaves < T::kWaves, "one more wave fetches the column scales");
+        auto issue_scales = [&](int c) __attribute__((always_inline)) {
+            const int kb0 = c * 4;
+            constexpr uint32_t kSz = sizeof(ScaleT);
+            if (kb0 >= KB) return;
+            if (wave < kScaleWaves) {
+                const v4u rs = buffer_rsrc(tileSA + kb0, (uint32_t)(ti.valid * SP - kb0) * kSz);
+                if (kE8)
+                    load_lds_4(rs, offSA, &smSA[c & 1][wave * 64]);
+                else
+                    load_lds_16(rs, offSA, &smSA[c & 1][wave * 64 * 4]);
+            } else if (wave == kScaleWaves) {
+                load_lds_4(buffer_rsrc(tileSB + kb0, (uint32_t)(vnb * SP - kb0) * kSz),
+                           lane < (kE8 ? 1 : 4) * vnb ? offSB : 0xffffff00u, &smSB[c & 1][0]);
+            }
+        };
+
+        // ---- fragment reads.  Sub-tile row i of wave row wm covers tile rows
+        // [16 (WAVES_M i + wm), +16): the wave rows interleave in 16-row steps, so
+        // a partial tile (a masked group's last rows, a ragged M) leaves work on
+        // every wave.  Every row r a lane reads is lr plus a multiple of 16, so
+        // r & 7 == lr & 7 and the swizzled chunk offsets are per-lane constants;
+        // sub-tile i (or j) only adds a multiple of 16 rows (an immediate).
+        static_assert(T::WN % 16 == 0, "wave column offsets keep the row swizzle");
+        constexpr int kRowStep = 16 * T::WAVES_M;
+        const int chunk_lo = (lg ^ (lr & 7)) << 4, chunk_hi = ((lg + 4) ^ (lr & 7)) << 4;
+        const int fragA = (16 * wm + lr) * 128, fragB = (wcol + lr) * 128;
+        const int srow = 16 * wm + lr;
+        // column-scale block of sub-tile j, relative to the tile's first one
+        int sblk[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) sblk[j] = (int)((ti.n0 + wcol + 16 * j) >> 7) - nb0;
+        auto frag = [&](const uint8_t* p) __attribute__((always_inline)) {
+            return join(*reinterpret_cast<const v4u*>(p + chunk_lo), *reinterpret_cast<const v4u*>(p + chunk_hi));
+        };
+
+        v4f acc[T::TM][T::TN];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        v8i bf[T::TN];
+
+        // Sub-tile rows [i0, i1) of the wave tile for the K block kb on stage st.
+        // With kSkip, rows that hold no valid row of the tile are skipped.
+        auto mma_rows = [&](auto skip, int kb, int st, int i0, int i1) __attribute__((always_inline)) {
+            constexpr bool kSkip = decltype(skip)::value;
+            const uint8_t* stA = smA + st * T::kStageA + fragA;
+            if constexpr (kE8) {
+                // exponent chunks: one 4-byte word per row / column block
+                const uint8_t* eSA = reinterpret_cast<const uint8_t*>(smSA[(kb >> 2) & 1]) + (kb & 3);
+                const uint8_t* eSB = reinterpret_cast<const uint8_t*>(smSB[(kb >> 2) & 1]) + (kb & 3);
+                int e_b[T::kOneScaleB ? 1 : T::TN];
+#pragma unroll
+                for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) e_b[j] = eSB[sblk[j] * 4];
+#pragma unroll
+                for (int i = i0; i < i1; ++i) {
+                    if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
+                    const v8i af = frag(stA + i * kRowStep * 128);
+                    const int e_a = eSA[(srow + kRowStep * i) * 4];
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j)
+                        acc[i][j] = mfma_block_e8(bf[j], af, acc[i][j], e_b[T::kOneScaleB ? 0 : j], e_a);
+                }
+            } else {
+                const float* sSA = &smSA[(kb >> 2) & 1][kb & 3];
+                const float* sSB = &smSB[(kb >> 2) & 1][kb & 3];
+                float s_b[T::kOneScaleB ? 1 : T::TN];
+#pragma unroll
+                for (int j = 0; j < (T::kOneScaleB ? 1 : T::TN); ++j) s_b[j] = sSB[sblk[j] * 4];
+#pragma unroll
+                for (int i = i0; i < i1; ++i) {
+                    if (kSkip && 16 * wm + kRowStep * i >= ti.valid) continue;
+                    const v8i af = frag(stA + i * kRowStep * 128);
+                    const float s_a = sSA[(srow + kRowStep * i) * 4];
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j)
+                        acc[i][j] += (s_a * s_b[T::kOneScaleB ? 0 : j]) * mfma_block(bf[j], af);
+                }
+            }
+        };
+
+        // Loads a wave issues after the ones a barrier waits for (see `step`),
+        // counted for the wave that issues the fewest B loads.
+        constexpr int kAfter = T::kLoadsA + T::kLoadsBMin;
+        static_assert(T::kLoadsA % 2 == 0 && kAfter < 64, "A slab halves, vmcnt range");
+
+        // One K block kb on stage st (= kb & 1), in two halves separated by a
+        // barrier.  The step starts by reading its B fragments (B slab of kb);
+        // the first half multiplies the A rows [0, BM/2), the second half the rows
+        // [BM/2, BM).  A slab load is issued as soon as the barrier that frees its
+        // buffer has passed:
+        //   after the mid barrier: A rows [0, BM/2) and the B slab of block kb+2
+        //     (their buffers held those of kb);
+        //   after the end barrier: A rows [BM/2, BM) of block kb+2.
+        // So every load has one and a half steps to land.  Loads of a wave
+        // complete in issue order; a barrier publishes what it needs by waiting
+        // until at most the loads issued after those (kAfter) remain.  Scale
+        // chunk loads (some waves, every fourth step) only make a wait stricter.
+        auto step = [&](auto skip, int kb, int st) __attribute__((always_inline)) {
+            const uint8_t* stB = smB + st * T::kStageB + fragB;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) bf[j] = frag(stB + j * 16 * 128);
+            mma_rows(skip, kb, st, 0, T::TM / 2);
+            wait_vmcnt_lgkm0<kAfter>();  // A rows [BM/2, BM) of kb
+            lds_barrier();
+            issue_a(kb + 2, st, 0, T::kLoadsA / 2);
+            issue_b(kb + 2, st);
+            if ((kb & 3) == 0) issue_scales((kb >> 2) + 1);
+            mma_rows(skip, kb, st, T::TM / 2, T::TM);
+            wait_vmcnt_lgkm0<kAfter>();  // A rows [0, BM/2) and B of kb+1
+            lds_barrier();
+            issue_a(kb + 2, st, T::kLoadsA / 2, T::kLoadsA);
+        };
+
+        // Prologue: blocks 0 and 1 of A rows [0, BM/2) and of B, A rows
+        // [BM/2, BM) of block 0 and scale chunk 0 land and are published; A rows
+        // [BM/2, BM) of block 1 go last, as in the steady state, so that the
+        // first waits count the same loads.
+        issue_scales(0);
+        issue_a(0, 0, 0, T::kLoadsA);
+        issue_b(0, 0);
+        issue_a(1, 1, 0, T::kLoadsA / 2);
+        issue_b(1, 1);
+        wait_vmcnt<0>();
+        lds_barrier();
+        issue_a(1, 1, T::kLoadsA / 2, T::kLoadsA);
+
+        auto k_loop = [&](auto skip) __attribute__((always_inline)) {
+            for (int kb = 0; kb < KB; kb += 2) {
+                step(skip, kb, 0);
+                if (kb + 1 < KB) step(skip, kb + 1, 1);
+            }
+        };
+        // A masked tile with rows past its group's count runs a copy of the loop
+        // that skips sub-tile rows without a valid row.  With fp32 scales full
+        // tiles keep the branch-free loop, whose schedule is faster; with E8M0
+        // scales one skipping loop serves every tile (measured faster).
+        if constexpr (kForm == Form::Masked && kE8) {
+            k_loop(std::true_type{});
+        } else if constexpr (kForm == Form::Masked) {
+            if (ti.valid < T::BM)
+                k_loop(std::true_type{});
+            else
+                k_loop(std::false_type{});
+        } else {
+            k_loop(std::false_type{});
+        }
+
+        // ---- epilogue
+        wait_vmcnt<0>();  // the empty loads of the last steps have retired
+        lds_barrier();
+        store_tile<T, kForm>(acc, smem, tid, wm, wcol, lr, lg, ti, C, D, N);
+        if constexpr (!kMixed) {
+            break;
+        } else {
+            if ((int64_t)ti.n0 + T::BN < N) {
+                ti.n0 += T::BN;
+            } else {
+                ti.n0 = 0;
+                if (!block_group(aux, G, ti.g, lane, ti)) break;
+            }
+            lds_barrier();  // the staged tile has been stored before the next pass loads
+        }
+    }
 }
 
 template <class T, Form kForm, bool kE8>
@@ -630,6 +667,15 @@ static dg_status launch_tiled(const GemmArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_kernel<T, kForm, kE8>), dim3((unsigned)grid), dim3(T::kThreads), 0, stream,
                        a.A, a.sa, a.B, a.sb, a.D, a.aux, a.C, a.rows, a.N, a.K, a.G, (int)m_blocks,
                        (int)n_blocks);
+    if constexpr (kForm == Form::Contiguous) {
+        // Blocks whose rows carry more than one valid id: one workgroup per
+        // 128-row block, which exits at once unless its block is mixed.  The
+        // ordinary launch above stays free of that rare case's code.
+        if (launched() != DG_OK) return DG_ERR_HIP;
+        hipLaunchKernelGGL((gemm_kernel<T, kForm, kE8, true>), dim3((unsigned)m_blocks), dim3(T::kThreads),
+                           0, stream, a.A, a.sa, a.B, a.sb, a.D, a.aux, a.C, a.rows, a.N, a.K, a.G,
+                           (int)m_blocks, (int)n_blocks);
+    }
     return launched();
 }
 

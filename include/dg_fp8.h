@@ -89,9 +89,10 @@ dg_status dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sa,
  * Row r is computed with B[g], sb[g] for g = grouped_layout[r] when
  * 0 <= g < G; any other row (padding, id -1) is not written.  Groups are
  * padded to 128 rows, so M_sum % 128 == 0 and each aligned block of 128 rows
- * holds at most one group id >= 0; a block that mixes ids has only the rows
- * of one of them written.  The page's kernel takes the same per-row int
- * array (grouped_layout) and adds per-group offsets in its scheduler.
+ * normally holds one group id >= 0; a block whose rows carry several ids is
+ * computed once per id (each pass costs a whole block's work), so every row
+ * still gets its own group's B.  The page's kernel takes the same per-row
+ * int array (grouped_layout) and adds per-group offsets in its scheduler.
  * Sizes: M_sum >= 0, G >= 1, N and K as for the dense form. */
 dg_status dg_fp8_gemm_grouped_contiguous(const uint8_t* A, const float* sa,
                                          const uint8_t* B, const float* sb,

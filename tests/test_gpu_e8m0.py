@@ -176,6 +176,19 @@ def test_contiguous_e8m0_parity(orc, sizes):
     _check_full(orc, contiguous_case(len(sizes), 264, 384, 7, sizes=sizes))
 
 
+def test_contiguous_e8m0_mixed_blocks_route_every_id(orc):
+    # blocks whose rows carry several valid ids, across several column tiles
+    case = contiguous_case(3, 600, 256, 9, sizes=[128, 128, 128])
+    lay = case.layout.clone()
+    lay[5:9] = 2
+    lay[70:72] = 1
+    lay[200:210] = 0
+    lay[211] = -1
+    case.layout = lay
+    got = _check_full(orc, case)
+    assert (got[211] == 0xFFFF).all()
+
+
 @pytest.mark.parametrize("masked", [[0, 200, 37, 129], [1, 0, 128, 2]])
 def test_masked_e8m0_parity(orc, masked):
     _check_full(orc, masked_case(len(masked), 256, 392, 640, 9, masked=masked))

@@ -168,23 +168,25 @@ def test_contiguous_split_tiles(orc, sizes):
                                      sizes=sizes))
 
 
-def test_contiguous_mixed_block_routes_largest_id(orc):
-    # a 128-row block that mixes two valid ids routes only the rows of the
-    # larger one; the other rows of that block stay untouched
+def test_contiguous_mixed_blocks_route_every_id(orc):
+    # a 128-row block whose rows carry several valid ids is run once per id,
+    # so every row is computed with its own group's B, as the oracle does;
+    # padding rows (-1) and ids outside [0, G) inside such blocks stay
+    # untouched
     case = contiguous_case(3, 136, 256, seed=21, sizes=[128, 128, 128])
     lay = case.layout.clone()
     lay[140:150] = 0    # block 1 (group 1) with some rows of group 0
+    lay[150:152] = -1   # and two padding rows
     lay[260:270] = 2    # block 2 is group 2 already: no change in routing
-    lay[10:20] = 2      # block 0 (group 0) with rows of group 2: group 2 wins
+    lay[10:20] = 2      # block 0 (group 0) with rows of group 2 ...
+    lay[30:33] = 1      # ... and of group 1: three passes
+    lay[40] = 3         # an id past G is not routed
     case.layout = lay
     qa, sa, qb, sb = _prepared(orc, case)
     got = _run(case, qa, sa, qb, sb).reshape(-1, case.N)
     ref = _oracle_full(orc, case, qa, sa, qb, sb).reshape(-1, case.N)
-    routed = np.zeros(case.M, bool)
-    routed[10:20] = True            # block 0: only the group-2 rows
-    routed[128:140] = True          # block 1: group-1 rows only
-    routed[150:256] = True
-    routed[256:384] = True          # block 2: all group 2
+    routed = ((lay >= 0) & (lay < 3)).numpy()
+    assert (~routed).sum() == 3
     assert (got[~routed] == 0xFFFF).all()
     assert_close_bf16(got[routed], ref[routed], "mixed blocks")
 
