@@ -176,6 +176,12 @@ def test_contiguous_e8m0_parity(orc, sizes):
     _check_full(orc, contiguous_case(len(sizes), 264, 384, 7, sizes=sizes))
 
 
+def test_e8m0_with_more_slots_than_cus(orc):
+    _check_full(orc, dense_case(4352, 4352, 256, seed=82))
+    mm = np.random.default_rng(83).integers(0, 257, 70).astype(np.int32)
+    _check_full(orc, masked_case(70, 256, 2048, 256, seed=83, masked=mm.tolist()))
+
+
 def test_contiguous_e8m0_mixed_blocks_route_every_id(orc):
     # blocks whose rows carry several valid ids, across several column tiles
     case = contiguous_case(3, 600, 256, 9, sizes=[128, 128, 128])

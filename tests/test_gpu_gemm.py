@@ -254,6 +254,33 @@ def test_epilogue_rounding_is_exact(orc, monkeypatch):
         assert np.array_equal(got, ref), tile
 
 
+def test_launches_with_more_slots_than_cus(orc):
+    """Launches with more tile slots than the device has CUs, in full: 289
+    dense tiles, about 600 contiguous tiles with a mixed block and padding
+    blocks, and 560 masked slots over 70 groups, some of them empty."""
+    _check_full(orc, dense_case(4352, 4352, 256, seed=77))
+    case = contiguous_case(5, 4096, 256, seed=78, m_lo=600, m_hi=1100)
+    lay = case.layout.clone()
+    lay[5:9] = (int(lay[0]) + 1) % 5   # one mixed block
+    case.layout = lay
+    _check_full(orc, case)
+    mm = np.random.default_rng(79).integers(0, 257, 70).astype(np.int32)
+    mm[::9] = 0
+    _check_full(orc, masked_case(70, 256, 2048, 256, seed=79, masked=mm.tolist()))
+
+
+def test_acc_with_more_slots_than_cus(orc):
+    M, N, K = 4352, 4352, 256
+    case = dense_case(M, N, K, seed=80)
+    qa, sa, qb, sb = _prepared(orc, case)
+    C = (np.random.default_rng(81).standard_normal((M, N)) * np.sqrt(K)).astype(np.float32)
+    D = torch.full((M, N), SENTINEL, dtype=torch.int16, device="cuda")
+    dg.dg_fp8_gemm_nt_acc(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), to_dev(C), D)
+    torch.cuda.synchronize()
+    check_call(D.cpu().numpy().view(np.uint16), orc.gemm_nt_acc(qa, sa, qb, sb, C),
+               np.arange(M), "acc, 289 tiles")
+
+
 @pytest.mark.parametrize("tile", ["256x256", "256x224", "256x192", "256x160", "128x256", "128x128", "128x64", "128x32", None])
 @pytest.mark.parametrize("M,N,K", [(300, 488, 384), (64, 256, 128), (512, 520, 256)])
 def test_dense_acc_parity(orc, monkeypatch, tile, M, N, K):
