@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import fp8_block_scaled_gemm_amd as dg
-from fp8_block_scaled_gemm_amd.inputs import dense_case, masked_case
+from fp8_block_scaled_gemm_amd.inputs import contiguous_case, dense_case, masked_case
 from tests.gpu_util import SENTINEL, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -27,18 +27,38 @@ def _operands(orc, case):
     return to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
 
 
-@pytest.mark.parametrize("form", ["dense", "masked"])
+@pytest.mark.parametrize("form", ["dense", "masked", "contiguous", "dense_acc"])
 def test_graph_replays_match_eager(orc, form):
-    if form == "dense":
+    extra = ()
+    if form in ("dense", "dense_acc"):
         case = dense_case(300, 520, 768, seed=91)
         call = dg.dg_fp8_gemm_nt
         shape = (case.M, case.N)
-    else:
+        if form == "dense_acc":
+            call = dg.dg_fp8_gemm_nt_acc
+            C = np.random.default_rng(93).standard_normal(shape).astype(np.float32) * 20
+            extra = (to_dev(C),)
+    elif form == "masked":
         case = masked_case(3, 200, 264, 640, 92, masked=[150, 0, 200])
         call = dg.dg_fp8_gemm_grouped_masked
         shape = (case.G, case.M, case.N)
+        extra = (to_dev(case.masked_m.numpy()),)
+    else:
+        # one block mixes two ids: the call's second launch has work too
+        case = contiguous_case(3, 264, 384, 94, sizes=[128, 200, 100])
+        lay = case.layout.clone()
+        lay[3:7] = 2
+        case.layout = lay
+        call = dg.dg_fp8_gemm_grouped_contiguous
+        shape = (case.M, case.N)
+        extra = (to_dev(case.layout.numpy()),)
     A, SA, B, SB = _operands(orc, case)
-    extra = (to_dev(case.masked_m.numpy()),) if form == "masked" else ()
+    if form == "dense_acc":
+        # the binding takes C before D
+        acc_call = call
+        C_dev = extra[0]
+        call = lambda a, sa, b, sb, d: acc_call(a, sa, b, sb, C_dev, d)  # noqa: E731
+        extra = ()
 
     eager = torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda")
     call(A, SA, B, SB, eager, *extra)
