@@ -107,6 +107,15 @@ def test_dense_tile_shapes(orc, monkeypatch, tile, M, N, K):
     _check_full(orc, dense_case(M, N, K, seed=M + N + K))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (40, 24, 1 << 20),     # 8192 K blocks: long K loop, per-lane offsets near 2^28
+    (3, 1 << 20, 128),     # 4096 column tiles: large column offsets into B and D
+    (1 << 17, 8, 256),     # 512 row tiles of a single 8-column group
+])
+def test_dense_extreme_extents(orc, M, N, K):
+    _check_full(orc, dense_case(M, N, K, seed=M + N % 1000 + K % 1000, name=f"dense_{M}x{N}x{K}"))
+
+
 def test_dense_parity_scaled_rows(orc):
     """Rows with very different magnitudes: per-row scales span 2^-20..2^20."""
     case = dense_case(200, 264, 512, seed=5)
