@@ -354,7 +354,9 @@ __device__ __forceinline__ void store_tile(v4f (&acc)[T::TM][T::TN], uint8_t* sm
     }
     __syncthreads();
     static_assert((T::BM * kChunks) % T::kThreads == 0, "whole passes over the output tile");
-#pragma unroll 4
+    // fully unrolled (the accumulators are dead by now): every pass's LDS
+    // read can be in flight before the first store waits for its data
+#pragma unroll
     for (int q = tid; q < T::BM * kChunks; q += T::kThreads) {
         const int row = q / kChunks, c = q % kChunks;
         const int64_t col = ti.n0 + c * 8;
